@@ -1,0 +1,169 @@
+/*
+ * sparse_attn.h -- C ABI of the MI355X (gfx950) sparse latent attention library
+ * (libsparse_attn.so).
+ *
+ * The operations are those of DeepSeek-V4.1's sparse latent attention as the
+ * following web pages describe them (cited by page title and section):
+ *   [ATTEND]  "DeepSeek V4.1 ... attention / attend" -- get_window_topk_idxs,
+ *             the sparse_attn kernel and its wrapper.
+ *   [QLAT]    "DeepSeek V4.1 ... attention / query-latent" -- Attention.forward
+ *             (concatenation of window and compressed indices), Indexer tail.
+ *   [ATTN-RS] "Module attn" rustdoc (DeepSeek-V4.1 reference, ratio-0
+ *             attention) -- precision contract, ring-cache worked example,
+ *             act_quant_inplace, pow2_ceil, sparse_attn, window_topk_idxs.
+ *
+ * Conventions for every entry point:
+ *   - bf16 tensors are passed as uint16_t bit patterns; f32 as float.
+ *   - Every tensor pointer is a DEVICE pointer (HIP device memory or memory the
+ *     device can address), tensors are dense row-major (C order).  The caller
+ *     owns all memory; the library allocates nothing, keeps no pointer after
+ *     return and holds no mutable global state, so calls from several host
+ *     threads are safe.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *     is enqueued asynchronously on it; buffers must stay alive until the stream
+ *     reaches that point.  Faults during execution surface at the caller's next
+ *     synchronisation, not in the return code.
+ *   - Return codes are synchronous argument checks plus the launch status:
+ *       SA_OK, SA_ERR_NULL (null pointer where the sizes need data),
+ *       SA_ERR_SHAPE (negative size, bad stride or block multiple, workspace
+ *       too small), SA_ERR_UNSUPPORTED (a case the pages do not define or a
+ *       head dim outside {64, 128, 256, 512}), SA_ERR_HIP (a HIP launch
+ *       failed).  Nothing is enqueued when a check fails.
+ *   - Sizes that make a call empty (zero rows/queries) return SA_OK and enqueue
+ *     nothing.
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SA_OK = 0,
+    SA_ERR_NULL = 1,
+    SA_ERR_SHAPE = 2,
+    SA_ERR_UNSUPPORTED = 3,
+    SA_ERR_HIP = 4
+} sa_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *sa_status_string(sa_status status);
+
+/* ------------------------------------------------------------------------
+ * Window slot selection -- [ATTEND] get_window_topk_idxs, [ATTN-RS]
+ * window_topk_idxs ("([queries][cols], cols)").
+ *
+ * Host-only shape query.  start_pos == 0 (prefill): rows = seqlen,
+ * cols = min(seqlen, window).  start_pos > 0 (decode): rows = 1, cols = window,
+ * and seqlen must be 1 (a chunk starting after position 0 is not defined on the
+ * pages: SA_ERR_UNSUPPORTED).
+ */
+sa_status sa_window_topk_idxs_shape(int32_t window, int32_t seqlen, int64_t start_pos,
+                                    int32_t *rows, int32_t *cols);
+
+/* Writes the window slot lists into idx (device, int32) laid out
+ * [bsz][rows][row_stride]; only the first `cols` entries of each row are
+ * written, so the lists can go straight into the leading columns of a wider
+ * index buffer (row_stride >= cols, else SA_ERR_SHAPE).
+ *   Prefill: query p lists the chunk positions max(0, p-window+1) + j,
+ *            j < cols, with -1 where that position is past p.
+ *   Decode:  the ring listed oldest first -- slots (start_pos % window + 1 + j)
+ *            % window -- with -1 for slots above start_pos (ring still
+ *            filling).  The newest token's slot comes last.
+ * The same rows are written for every batch element. */
+sa_status sa_window_topk_idxs(int32_t window, int32_t bsz, int32_t seqlen, int64_t start_pos,
+                              int32_t *idx, int64_t row_stride, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Compressed-index concatenation -- [QLAT] Attention.forward concatenates the
+ * compressed indices after the window ones; the Indexer tail shifts reachable
+ * positions by the window-row count and leaves unreachable ones at -1.
+ *
+ * For r < n_rows, j < kc:  idx[r*row_stride + col0 + j] =
+ *     cidx[r*kc + j] < 0 ? -1 : cidx[r*kc + j] + offset.
+ * idx, cidx: device int32.  row_stride >= col0 + kc and offset >= 0, else
+ * SA_ERR_SHAPE.  Other columns of idx are left untouched. */
+sa_status sa_append_compressed_idxs(int32_t *idx, int64_t row_stride, int32_t col0,
+                                    const int32_t *cidx, int64_t n_rows, int32_t kc,
+                                    int32_t offset, void *stream);
+
+/* ------------------------------------------------------------------------
+ * fp8 round trip -- [ATTN-RS] act_quant_inplace, pow2_ceil, "Precision".
+ *
+ * x: device bf16 [n_rows][row_len], modified in place.  For every block of 32
+ * contiguous values along a row: amax = max|x| floored at 1e-4,
+ * scale = 2^ceil(log2(amax / 448)) (f32 quotient, power-of-two ceiling from
+ * the IEEE fields), each value rounded to OCP e4m3 (nearest, ties to even,
+ * clamped to +-448) at that scale, multiplied back and stored as bf16 (exact:
+ * e4m3 times a power of two).  row_len must be a positive multiple of 32 (else
+ * SA_ERR_SHAPE).  Bit-exact; idempotent. */
+sa_status sa_act_quant_fp8_inplace(uint16_t *x, int64_t n_rows, int32_t row_len, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Sparse latent attention -- [ATTEND] sparse_attn_kernel / sparse_attn,
+ * [ATTN-RS] sparse_attn ("per query and head, softmax over the gathered rows
+ * plus the sink (denominator only), all in f32; output bf16").
+ *
+ *   q    [b][s][h][d]  bf16   queries (already rotated by the caller)
+ *   kv   [b][rows][d]  bf16   latent rows, each serving as key and value for
+ *                             every head (one row per token, shared by heads)
+ *   sink [h]           f32    per-head sink logit
+ *   idx  [b][s][topk]  int32  rows of kv[b] that query (b, s) attends to;
+ *                             -1 = skip.  A row listed twice counts twice and
+ *                             the order within a list does not matter.
+ *   out  [b][s][h][d]  bf16   result
+ * For each (b, s, head i), with the valid entries t of the query's list:
+ *   out = sum_t e^(x_t) kv[idx_t] / (sum_t e^(x_t) + e^(sink_i)),
+ *   x_t = scale * <q_i, kv[idx_t]>;
+ * a query with no valid entry outputs zeros.  Arithmetic: bf16 products with
+ * f32 accumulation, f32 softmax; the attention weights are rounded to bf16 for
+ * the weighted sum of rows (the pages' kernel does the same), result rounded to
+ * nearest-even bf16.  Agreement with the exact f32 definition: within
+ * max(2 bf16 ulp of the result, 1e-2) per element.
+ *
+ * Index entries outside {-1} U [0, rows) are a caller error; the kernels treat
+ * them as -1 (one unsigned compare), so no out-of-bounds access results.
+ * scale is always explicit (the pages' default is d^-0.5).
+ * d must be one of {64, 128, 256, 512} (SA_ERR_UNSUPPORTED otherwise); h >= 1.
+ * topk = 0 is allowed (zeros out).  rows = 0 is allowed only with topk
+ * entries all -1.
+ *
+ * workspace: device scratch of at least sa_sparse_attn_workspace_bytes(b, s, h,
+ * d, topk) bytes (may be NULL when that is 0).  The library picks the kernel
+ * variant deterministically from (b*s, h, d, topk) and the device's compute-unit
+ * count; the workspace holds the f32 partial results of the split-topk decode
+ * variant.  Results are deterministic: the same inputs give bitwise identical
+ * outputs. */
+size_t sa_sparse_attn_workspace_bytes(int64_t b, int64_t s, int32_t h, int32_t d, int32_t topk);
+
+sa_status sa_sparse_attn(const uint16_t *q, const uint16_t *kv, const float *sink,
+                         const int32_t *idx, int64_t b, int64_t s, int32_t h, int32_t d,
+                         int64_t rows, int32_t topk, float scale, uint16_t *out,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* Same operation with the variant forced (for tests and measurement):
+ *   heads_per_wg in {16, 32, 64} (16 heads per wavefront; 0 = automatic),
+ *   row_waves in {1, 2, 4} (wavefronts splitting the index list inside one
+ *   workgroup; 0 = automatic), splits >= 1 (workgroups splitting the index
+ *   list, combined in f32 through the workspace; 0 = automatic).
+ * A workgroup has (heads_per_wg / 16) * row_waves wavefronts, at most 4;
+ * splits > 1 requires row_waves == 1 (else SA_ERR_UNSUPPORTED).  The
+ * workspace must hold sa_sparse_attn_workspace_bytes_ex() bytes. */
+size_t sa_sparse_attn_workspace_bytes_ex(int64_t b, int64_t s, int32_t h, int32_t d, int32_t topk,
+                                         int32_t heads_per_wg, int32_t row_waves, int32_t splits);
+
+sa_status sa_sparse_attn_ex(const uint16_t *q, const uint16_t *kv, const float *sink,
+                            const int32_t *idx, int64_t b, int64_t s, int32_t h, int32_t d,
+                            int64_t rows, int32_t topk, float scale, uint16_t *out,
+                            void *workspace, size_t workspace_bytes, void *stream,
+                            int32_t heads_per_wg, int32_t row_waves, int32_t splits);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

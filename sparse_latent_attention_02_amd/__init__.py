@@ -1,0 +1,167 @@
+"""MI355X (gfx950) sparse latent attention -- Python binding of libsparse_attn.so.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C ABI
+declared in ``include/sparse_attn.h``.  PyTorch supplies device memory and the
+current stream.  There is no CPU fallback: if the library is missing or the
+tensors are not on a GPU, the calls raise.
+
+Names follow the C ABI:
+  window_topk_idxs / window_topk_idxs_shape -- window slot lists
+  append_compressed_idxs                   -- compressed positions after the window
+  act_quant_fp8_                           -- fp8 (e4m3) round trip of bf16 rows, in place
+  sparse_attn                              -- the attention itself
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime this library then shares
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsparse_attn.so")
+_lib = None
+
+SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_UNSUPPORTED, SA_ERR_HIP = 0, 1, 2, 3, 4
+
+
+class SparseAttnError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        name = lib().sa_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{fn}: {name}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m sparse_latent_attention_02_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, i64, f32, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+        L.sa_status_string.argtypes = [ctypes.c_int]
+        L.sa_status_string.restype = ctypes.c_char_p
+        L.sa_window_topk_idxs_shape.argtypes = [i32, i32, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+        L.sa_window_topk_idxs.argtypes = [i32, i32, i32, i64, vp, i64, vp]
+        L.sa_append_compressed_idxs.argtypes = [vp, i64, i32, vp, i64, i32, i32, vp]
+        L.sa_act_quant_fp8_inplace.argtypes = [vp, i64, i32, vp]
+        L.sa_sparse_attn_workspace_bytes.argtypes = [i64, i64, i32, i32, i32]
+        L.sa_sparse_attn_workspace_bytes.restype = sz
+        L.sa_sparse_attn_workspace_bytes_ex.argtypes = [i64, i64, i32, i32, i32, i32, i32, i32]
+        L.sa_sparse_attn_workspace_bytes_ex.restype = sz
+        L.sa_sparse_attn.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i64, i32, f32, vp, vp, sz, vp]
+        L.sa_sparse_attn_ex.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i64, i32, f32, vp, vp, sz, vp,
+                                        i32, i32, i32]
+        for fn in ("sa_window_topk_idxs_shape", "sa_window_topk_idxs", "sa_append_compressed_idxs",
+                   "sa_act_quant_fp8_inplace", "sa_sparse_attn", "sa_sparse_attn_ex"):
+            getattr(L, fn).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != SA_OK:
+        raise SparseAttnError(fn, status)
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def window_topk_idxs_shape(window: int, seqlen: int, start_pos: int) -> tuple[int, int]:
+    r, c = ctypes.c_int32(), ctypes.c_int32()
+    _check("sa_window_topk_idxs_shape",
+           lib().sa_window_topk_idxs_shape(window, seqlen, start_pos, ctypes.byref(r), ctypes.byref(c)))
+    return r.value, c.value
+
+
+def window_topk_idxs(window: int, bsz: int, seqlen: int, start_pos: int, out: torch.Tensor | None = None,
+                     device=None, stream=None) -> torch.Tensor:
+    """int32 [bsz][rows][cols] window slot lists (-1 = empty slot).  With ``out``
+    ([bsz][rows][stride], stride >= cols) the lists fill its leading columns."""
+    rows, cols = window_topk_idxs_shape(window, seqlen, start_pos)
+    if out is None:
+        out = torch.empty((bsz, rows, cols), dtype=torch.int32, device=device or "cuda")
+    _dev(out, "out", torch.int32)
+    if out.dim() != 3 or out.shape[0] != bsz or out.shape[1] != rows:
+        raise ValueError(f"out must be [{bsz}][{rows}][>= {cols}], got {tuple(out.shape)}")
+    _check("sa_window_topk_idxs",
+           lib().sa_window_topk_idxs(window, bsz, seqlen, start_pos, out.data_ptr(), out.shape[-1],
+                                     _stream(stream)))
+    return out
+
+
+def append_compressed_idxs(idx: torch.Tensor, col0: int, cidx: torch.Tensor, offset: int, stream=None) -> None:
+    """idx[..., col0 + j] = cidx[..., j] + offset (or -1 where cidx < 0), in place."""
+    _dev(idx, "idx", torch.int32)
+    _dev(cidx, "cidx", torch.int32)
+    kc = cidx.shape[-1]
+    n_rows = cidx.numel() // kc if kc else 0
+    if idx.numel() // idx.shape[-1] != n_rows and kc:
+        raise ValueError("idx and cidx have different row counts")
+    _check("sa_append_compressed_idxs",
+           lib().sa_append_compressed_idxs(idx.data_ptr(), idx.shape[-1], col0, cidx.data_ptr(), n_rows, kc,
+                                           offset, _stream(stream)))
+
+
+def act_quant_fp8_(x: torch.Tensor, stream=None) -> torch.Tensor:
+    """fp8 e4m3 round trip (block 32, power-of-two scale) of bf16 rows, in place."""
+    _dev(x, "x", torch.bfloat16)
+    row_len = x.shape[-1]
+    n_rows = x.numel() // row_len if row_len else 0
+    _check("sa_act_quant_fp8_inplace",
+           lib().sa_act_quant_fp8_inplace(x.data_ptr(), n_rows, row_len, _stream(stream)))
+    return x
+
+
+def workspace_bytes(b: int, s: int, h: int, d: int, topk: int, variant: tuple | None = None) -> int:
+    if variant is None:
+        return int(lib().sa_sparse_attn_workspace_bytes(b, s, h, d, topk))
+    return int(lib().sa_sparse_attn_workspace_bytes_ex(b, s, h, d, topk, *variant))
+
+
+def sparse_attn(q: torch.Tensor, kv: torch.Tensor, sink: torch.Tensor, idx: torch.Tensor, scale: float,
+                out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                variant: tuple | None = None, stream=None) -> torch.Tensor:
+    """q [b][s][h][d] bf16, kv [b][rows][d] bf16, sink [h] f32, idx [b][s][topk] int32 -> [b][s][h][d] bf16.
+
+    ``variant`` = (heads_per_wg, row_waves, splits) forces a kernel variant (0 = automatic)."""
+    _dev(q, "q", torch.bfloat16)
+    _dev(kv, "kv", torch.bfloat16)
+    _dev(sink, "sink", torch.float32)
+    _dev(idx, "idx", torch.int32)
+    b, s, h, d = q.shape
+    if kv.dim() != 3 or kv.shape[0] != b or kv.shape[2] != d:
+        raise ValueError(f"kv must be [{b}][rows][{d}], got {tuple(kv.shape)}")
+    if idx.dim() != 3 or idx.shape[0] != b or idx.shape[1] != s:
+        raise ValueError(f"idx must be [{b}][{s}][topk], got {tuple(idx.shape)}")
+    if sink.shape != (h,):
+        raise ValueError(f"sink must be [{h}]")
+    rows, topk = kv.shape[1], idx.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", torch.bfloat16)
+    need = workspace_bytes(b, s, h, d, topk, variant)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    args = (q.data_ptr(), kv.data_ptr(), sink.data_ptr(), idx.data_ptr(), b, s, h, d, rows, topk, float(scale),
+            out.data_ptr(), ws_ptr, ws_bytes, _stream(stream))
+    if variant is None:
+        _check("sa_sparse_attn", lib().sa_sparse_attn(*args))
+    else:
+        _check("sa_sparse_attn_ex", lib().sa_sparse_attn_ex(*args, *variant))
+    return out

@@ -1,0 +1,71 @@
+// sa_device.h -- device-side helpers shared by the gfx950 kernels of libsparse_attn.
+//
+// Vector types for MFMA operands, bf16 bit conversions, the direct global->LDS
+// copy (one 16-byte chunk per lane) and the explicit wait/barrier primitives the
+// gather pipeline relies on.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+#define SA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Round-to-nearest-even f32 -> bf16 bits (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Two f32 -> packed pair of bf16 (low half = a), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const SA_LDS void *p) {
+    return (uint32_t)(uintptr_t)p;
+}
+
+// Direct global -> LDS copy of one 16-byte chunk per lane (gfx950
+// global_load_lds_dwordx4).  The wave's 64 chunks land contiguously at the
+// wave-uniform LDS byte address `lds_base` (lane i at lds_base + 16 i).  Issued
+// through inline asm so that the compiler adds no waits of its own; completion
+// is tracked by the caller with wait_vmcnt_barrier().
+__device__ __forceinline__ void dma_16B(const void *src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds_base)
+                 : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding,
+// then barrier the workgroup (all LDS writes of completed copies visible).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+// Wait for this wave's LDS operations, then barrier the workgroup.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+}
+
+__device__ __forceinline__ float shfl_xor_f32(float v, int mask) {
+    return __shfl_xor(v, mask, 64);
+}
+
+}  // namespace sa

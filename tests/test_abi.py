@@ -1,0 +1,56 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads and exports
+every entry point include/sparse_attn.h declares; shape queries and argument
+checks that return before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import sparse_latent_attention_02_amd as sa
+    if not os.path.exists(sa.LIB_PATH):
+        from sparse_latent_attention_02_amd import build
+        build.build()
+    return sa.lib()
+
+
+def test_header_declares_the_boundary():
+    syms = declared_symbols()
+    for s in ("sa_window_topk_idxs", "sa_window_topk_idxs_shape", "sa_append_compressed_idxs",
+              "sa_act_quant_fp8_inplace", "sa_sparse_attn", "sa_sparse_attn_workspace_bytes",
+              "sa_status_string"):
+        assert s in syms
+
+
+def test_library_exports_every_declared_symbol(lib):
+    missing = [s for s in declared_symbols() if not hasattr(lib, s)]
+    assert not missing, missing
+
+
+def test_host_only_calls(lib):
+    import sparse_latent_attention_02_amd as sa
+    assert sa.window_topk_idxs_shape(8, 12, 0) == (12, 8)
+    assert sa.window_topk_idxs_shape(128, 1, 5000) == (1, 128)
+    with pytest.raises(sa.SparseAttnError):
+        sa.window_topk_idxs_shape(8, 3, 7)
+    assert lib.sa_status_string(3) == b"SA_ERR_UNSUPPORTED"
+    # argument checks fail before any device work
+    assert lib.sa_act_quant_fp8_inplace(None, 4, 33, None) == sa.SA_ERR_SHAPE
+    assert lib.sa_act_quant_fp8_inplace(None, 4, 32, None) == sa.SA_ERR_NULL
+    assert lib.sa_append_compressed_idxs(None, 4, 2, None, 3, 5, 0, None) == sa.SA_ERR_SHAPE
+    assert lib.sa_sparse_attn(None, None, None, None, -1, 1, 1, 64, 1, 1, 0.1, None, None, 0, None) == sa.SA_ERR_SHAPE
+    assert lib.sa_sparse_attn(None, None, None, None, 1, 1, 1, 96, 1, 1, 0.1, None, None, 0, None) == sa.SA_ERR_UNSUPPORTED
+    assert lib.sa_sparse_attn(None, None, None, None, 0, 1, 1, 64, 1, 1, 0.1, None, None, 0, None) == sa.SA_OK
+    assert lib.sa_sparse_attn_workspace_bytes(1, 1, 1, 96, 1) == 0
