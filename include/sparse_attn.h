@@ -104,6 +104,28 @@ sa_status sa_append_compressed_idxs(int32_t *idx, int64_t row_stride, int32_t co
 sa_status sa_act_quant_fp8_inplace(uint16_t *x, int64_t n_rows, int32_t row_len, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Ring-cache update -- [ATTN-RS] ring-cache worked example (12 prefill tokens
+ * into 8 slots leave slots 4..7 = tokens 4..7 and slots 0..3 = tokens 8..11;
+ * decode step 12 writes slot 4, step 13 slot 5) and "the KV row rounded
+ * through fp8 in place" of the module description; [QLAT] Attention.__init__
+ * (zero-initialised ring of window_size slots per batch element).
+ *
+ * rows: device bf16 [bsz][seqlen][d], the new KV rows for positions
+ * start_pos .. start_pos+seqlen-1; rounded through fp8 in place exactly as
+ * sa_act_quant_fp8_inplace does (prefill attends to the chunk itself).
+ * ring: device bf16, batch element b's ring is rows [b*ring_stride, b*ring_stride
+ * + window) of a [bsz][ring_stride][d] buffer (ring_stride >= window, so the ring
+ * can head a longer per-sequence KV buffer that also holds compressed rows);
+ * the chunk's last min(seqlen, window) rows are written to slots
+ * (position % window); other slots are untouched.
+ * d % 32 == 0 and ring_stride >= window (else SA_ERR_SHAPE); a chunk starting after position 0 must hold
+ * one row (else SA_ERR_UNSUPPORTED, as for the window lists).  Decode order: call
+ * this before building the window lists and attending, so the ring holds the
+ * new token. */
+sa_status sa_window_kv_update(uint16_t *ring, int64_t ring_stride, uint16_t *rows, int32_t bsz,
+                              int32_t window, int32_t d, int64_t start_pos, int32_t seqlen, void *stream);
+
+/* ------------------------------------------------------------------------
  * Sparse latent attention -- [ATTEND] sparse_attn_kernel / sparse_attn,
  * [ATTN-RS] sparse_attn ("per query and head, softmax over the gathered rows
  * plus the sink (denominator only), all in f32; output bf16").
@@ -145,22 +167,34 @@ sa_status sa_sparse_attn(const uint16_t *q, const uint16_t *kv, const float *sin
                          int64_t rows, int32_t topk, float scale, uint16_t *out,
                          void *workspace, size_t workspace_bytes, void *stream);
 
+/* Kernel variants of sa_sparse_attn_ex. */
+typedef enum {
+    SA_KERNEL_AUTO = 0,
+    /* one workgroup per (query, 64 heads); each wavefront holds 32 heads
+     * (over half the head dim at d = 512); 32-row multi-buffered stages */
+    SA_KERNEL_WIDE = 1,
+    /* one workgroup of four wavefronts per (query, 16 heads); 128-row stages
+     * whose rows the wavefronts split for the scores and whose head dim they
+     * split for the weighted sum (decode-sized batches) */
+    SA_KERNEL_DECODE = 2
+} sa_kernel;
+
 /* Same operation with the variant forced (for tests and measurement):
- *   heads_per_wg in {16, 32, 64} (16 heads per wavefront; 0 = automatic),
- *   row_waves in {1, 2, 4} (wavefronts splitting the index list inside one
- *   workgroup; 0 = automatic), splits >= 1 (workgroups splitting the index
- *   list, combined in f32 through the workspace; 0 = automatic).
- * A workgroup has (heads_per_wg / 16) * row_waves wavefronts, at most 4;
- * splits > 1 requires row_waves == 1 (else SA_ERR_UNSUPPORTED).  The
- * workspace must hold sa_sparse_attn_workspace_bytes_ex() bytes. */
+ *   kernel in sa_kernel (SA_KERNEL_AUTO = the automatic choice);
+ *   splits >= 1: the index list is cut into that many contiguous pieces, each
+ *   handled by its own workgroup, and the f32 partial results (running max,
+ *   running sum, unnormalised output) are combined by a second kernel through
+ *   the workspace; 0 = automatic.  Unknown kernels or negative splits give
+ *   SA_ERR_UNSUPPORTED.  The workspace must hold
+ *   sa_sparse_attn_workspace_bytes_ex() bytes (16-byte aligned). */
 size_t sa_sparse_attn_workspace_bytes_ex(int64_t b, int64_t s, int32_t h, int32_t d, int32_t topk,
-                                         int32_t heads_per_wg, int32_t row_waves, int32_t splits);
+                                         int32_t kernel, int32_t splits);
 
 sa_status sa_sparse_attn_ex(const uint16_t *q, const uint16_t *kv, const float *sink,
                             const int32_t *idx, int64_t b, int64_t s, int32_t h, int32_t d,
                             int64_t rows, int32_t topk, float scale, uint16_t *out,
                             void *workspace, size_t workspace_bytes, void *stream,
-                            int32_t heads_per_wg, int32_t row_waves, int32_t splits);
+                            int32_t kernel, int32_t splits);
 
 #ifdef __cplusplus
 }

@@ -9,6 +9,7 @@ Names follow the C ABI:
   window_topk_idxs / window_topk_idxs_shape -- window slot lists
   append_compressed_idxs                   -- compressed positions after the window
   act_quant_fp8_                           -- fp8 (e4m3) round trip of bf16 rows, in place
+  window_kv_update                         -- fp8 round trip of new rows + ring-cache write
   sparse_attn                              -- the attention itself
 """
 from __future__ import annotations
@@ -23,6 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libsparse_attn.so")
 _lib = None
 
 SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_UNSUPPORTED, SA_ERR_HIP = 0, 1, 2, 3, 4
+SA_KERNEL_AUTO, SA_KERNEL_WIDE, SA_KERNEL_DECODE = 0, 1, 2
 
 
 class SparseAttnError(RuntimeError):
@@ -47,15 +49,16 @@ def lib() -> ctypes.CDLL:
         L.sa_window_topk_idxs.argtypes = [i32, i32, i32, i64, vp, i64, vp]
         L.sa_append_compressed_idxs.argtypes = [vp, i64, i32, vp, i64, i32, i32, vp]
         L.sa_act_quant_fp8_inplace.argtypes = [vp, i64, i32, vp]
+        L.sa_window_kv_update.argtypes = [vp, i64, vp, i32, i32, i32, i64, i32, vp]
         L.sa_sparse_attn_workspace_bytes.argtypes = [i64, i64, i32, i32, i32]
         L.sa_sparse_attn_workspace_bytes.restype = sz
-        L.sa_sparse_attn_workspace_bytes_ex.argtypes = [i64, i64, i32, i32, i32, i32, i32, i32]
+        L.sa_sparse_attn_workspace_bytes_ex.argtypes = [i64, i64, i32, i32, i32, i32, i32]
         L.sa_sparse_attn_workspace_bytes_ex.restype = sz
         L.sa_sparse_attn.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i64, i32, f32, vp, vp, sz, vp]
         L.sa_sparse_attn_ex.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i64, i32, f32, vp, vp, sz, vp,
-                                        i32, i32, i32]
+                                        i32, i32]
         for fn in ("sa_window_topk_idxs_shape", "sa_window_topk_idxs", "sa_append_compressed_idxs",
-                   "sa_act_quant_fp8_inplace", "sa_sparse_attn", "sa_sparse_attn_ex"):
+                   "sa_act_quant_fp8_inplace", "sa_window_kv_update", "sa_sparse_attn", "sa_sparse_attn_ex"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -126,6 +129,23 @@ def act_quant_fp8_(x: torch.Tensor, stream=None) -> torch.Tensor:
     return x
 
 
+def window_kv_update(ring: torch.Tensor, rows: torch.Tensor, start_pos: int, window: int | None = None,
+                     stream=None) -> None:
+    """Rounds the new rows [bsz][seqlen][d] through fp8 in place and writes the
+    surviving ones into the ring at slot position % window.  ``ring`` is
+    [bsz][stride][d]; its first ``window`` rows per batch element (default: all
+    of them) form the ring."""
+    _dev(ring, "ring", torch.bfloat16)
+    _dev(rows, "rows", torch.bfloat16)
+    bsz, stride, d = ring.shape
+    window = stride if window is None else window
+    if rows.dim() != 3 or rows.shape[0] != bsz or rows.shape[2] != d:
+        raise ValueError(f"rows must be [{bsz}][seqlen][{d}], got {tuple(rows.shape)}")
+    _check("sa_window_kv_update",
+           lib().sa_window_kv_update(ring.data_ptr(), stride, rows.data_ptr(), bsz, window, d, start_pos,
+                                     rows.shape[1], _stream(stream)))
+
+
 def workspace_bytes(b: int, s: int, h: int, d: int, topk: int, variant: tuple | None = None) -> int:
     if variant is None:
         return int(lib().sa_sparse_attn_workspace_bytes(b, s, h, d, topk))
@@ -137,7 +157,7 @@ def sparse_attn(q: torch.Tensor, kv: torch.Tensor, sink: torch.Tensor, idx: torc
                 variant: tuple | None = None, stream=None) -> torch.Tensor:
     """q [b][s][h][d] bf16, kv [b][rows][d] bf16, sink [h] f32, idx [b][s][topk] int32 -> [b][s][h][d] bf16.
 
-    ``variant`` = (heads_per_wg, row_waves, splits) forces a kernel variant (0 = automatic)."""
+    ``variant`` = (kernel, splits) forces a kernel variant (see sa_kernel; 0 = automatic)."""
     _dev(q, "q", torch.bfloat16)
     _dev(kv, "kv", torch.bfloat16)
     _dev(sink, "sink", torch.float32)

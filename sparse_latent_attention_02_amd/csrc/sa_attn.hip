@@ -1,4 +1,5 @@
-// sa_attn.hip -- sparse latent attention for CDNA4 (gfx950).
+// sa_attn.hip -- sparse latent attention for CDNA4 (gfx950): the wide kernel,
+// the split combine and the dispatcher.
 //
 // Operation ("DeepSeek V4.1 ... attention / attend": sparse_attn_kernel and its
 // wrapper; "Module attn" rustdoc: sparse_attn): for every query and head, a
@@ -7,33 +8,37 @@
 // One latent row is both key and value and is shared by every head, so a
 // workgroup gathers each selected row into LDS once and all its heads use it.
 //
-// Kernel structure (one workgroup per (query, head group[, index split])):
+// Wide kernel: one workgroup per (query, group of 64 heads[, index split]);
+// each wavefront owns 32 heads, over the whole head dim up to d = 256 and over
+// half of it at d = 512 (a wavefront pair then sums its partial scores through
+// LDS before the softmax).
 //  1. compaction: the query's index entries are scanned and the valid ones
 //     (0 <= idx < rows) packed into an LDS list, so -1 entries cost no MFMA work
 //     and no traffic;
-//  2. gather: stages of 32 rows per row-wavefront are copied HBM -> LDS with the
-//     direct global->LDS path (16 B per lane, one 1 KiB row per wave instruction
-//     at d = 512), double-buffered so the copy of stage t+1 overlaps the maths
-//     of stage t; the 16-byte chunks of a row are XOR-swizzled by row so the
-//     MFMA operand reads below hit distinct LDS banks;
-//  3. scores: S^T[row][head] = K[row][:] . Q[head][:] on MFMA 16x16x32 bf16
-//     (A = 16 gathered rows from LDS, B = 16 heads of Q held in registers for
-//     the whole kernel), f32 accumulation;
-//  4. online softmax in the base-2 domain (scale * log2 e folded once): the
-//     accumulator layout puts one head per lane column, so the running max needs
-//     only two cross-lane steps and the running sum none until the end; the
-//     running max starts at the finite -1e30 of the pages' kernel, so a list
-//     with no valid entry yields zeros rather than NaN;
-//  5. O^T[d][head] += V^T[d][rows] . P^T[rows][head] on the same MFMA, with P
-//     rounded to bf16 straight from the score registers (no shuffle) and V^T read
-//     from LDS with the gfx950 transposing read ds_read_b64_tr_b16;
-//  6. sink fold, normalisation, bf16 store -- or, for split variants, f32
-//     partials (running max, sum, unnormalised O) combined by a second pass.
-//
-// Rows within a 16-row MFMA tile are visited in the order rho(m) (even rows,
-// then odd) so that the transposing reads of one half-wave touch distinct
-// banks under the swizzle; any row order is valid because each row's score and
-// its value travel together.
+//  2. gather: 32-row stages copied HBM -> LDS with the direct global->LDS path
+//     (16 B per lane, one 1 KiB row per wave instruction at d = 512),
+//     double-buffered so the copy of stage t+1 overlaps the maths of stage t.
+//     LDS rows are padded by 48 bytes, which keeps both operand reads of steps 3
+//     and 5 free of bank conflicts and makes every operand address a per-lane
+//     base plus an immediate;
+//  3. scores S^T[32 rows][32 heads] = K[rows][:] . Q[heads][:]^T on MFMA
+//     32x32x16 bf16 (A = gathered rows from LDS, B = the wave's Q held in
+//     registers for the whole kernel), f32 accumulation;
+//  4. online softmax in the base-2 domain (scale * log2 e folded once).  The
+//     accumulator layout puts one head per lane column, so the running max
+//     needs one cross-lane step.  The running max is only moved (and O, l
+//     rescaled) when a stage's max exceeds it by more than 2^8, so most stages
+//     skip the rescale; weights stay <= 256, well inside bf16's range.  It
+//     starts at the finite -1e30 of the pages' kernel, so a list with no valid
+//     entry yields zeros rather than NaN;
+//  5. O^T[d][head] += V^T[d][rows] . P^T[rows][head] on the same MFMA: P is
+//     rounded to bf16 straight from the score registers (its lane layout is the
+//     B operand's, up to a permutation of the contraction index that the V^T
+//     reads follow), V^T comes from LDS through the gfx950 transposing read
+//     ds_read_b64_tr_b16;
+//  6. sink fold, normalisation, bf16 staged through LDS and stored one row per
+//     wave instruction -- or, for split variants, f32 partials (running max,
+//     sum, unnormalised O) combined by a second pass.
 #include "sa_device.h"
 #include "../../include/sparse_attn.h"
 
@@ -43,8 +48,10 @@ namespace {
 
 using namespace sa;
 
-constexpr int kBlk = 32;        // index entries per row-wavefront per stage (two MFMA tiles)
-constexpr int kListCap = 2048;  // compacted entries held in LDS at once
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kListCap = 2048;        // compacted entries held in LDS at once
+constexpr float kRescaleSlack = 8.0f; // log2 units the reference max may lag behind
 
 struct AttnParams {
     const uint16_t *q;
@@ -54,10 +61,10 @@ struct AttnParams {
     uint16_t *out;
     float *part_o;   // [nq][n_sp][h][d] f32 (split variant only)
     float *part_ml;  // [nq][n_sp][h][2] f32: running max (log2 units), running sum
-    int64_t nq;      // b * s
-    int64_t s;       // queries per sequence
     int64_t rows;    // kv rows per sequence
-    int64_t total_wg;
+    int32_t nq;      // b * s
+    int32_t s;       // queries per sequence
+    int32_t total_wg;
     int32_t h;
     int32_t topk;
     int32_t n_hg;       // head groups
@@ -65,14 +72,6 @@ struct AttnParams {
     int32_t split_len;  // index entries per split
     float scale_log2;   // softmax scale * log2(e)
 };
-
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-    // XOR applied to the 16-byte chunk index of a row held in LDS
-    return D >= 128 ? (r & 15) : ((r >> 1) & 7);
-}
-
-__device__ __forceinline__ int rho(int m) { return m < 8 ? 2 * m : 2 * (m - 8) + 1; }
 
 __device__ __forceinline__ bf16x8_t lds_read_b128(const SA_LDS char *p) {
     return *reinterpret_cast<const SA_LDS bf16x8_t *>(p);
@@ -85,291 +84,552 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const SA_LDS char *p) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int D, int WH, int WR>
-struct Cfg {
-    static constexpr int NW = WH * WR;
-    static constexpr int NT = 64 * NW;
-    static constexpr int ROW_BYTES = 2 * D;
-    static constexpr int CH = D / 8;   // 16-byte chunks per row
-    static constexpr int KS = D / 32;  // k-steps of the score product
-    static constexpr int DT = D / 16;  // 16-wide d tiles of the output
-    static constexpr int ROWS_STAGE = kBlk * WR;
-    static constexpr int STAGE_BYTES = ROWS_STAGE * ROW_BYTES;
-    static constexpr int NBUF = WR <= 2 ? 2 : 1;
-    static constexpr int RPI = 1024 / ROW_BYTES;            // rows per copy instruction
-    static constexpr int INST_STAGE = STAGE_BYTES / 1024;   // copy instructions per stage
-    static constexpr int IPW = INST_STAGE / NW;             // ... per wavefront
-    static constexpr int KV_BYTES = NBUF * STAGE_BYTES;
-    static constexpr int PART_BYTES = WR > 1 ? NW * D * 64 : 0;  // f32 partials of all waves
-    static_assert(INST_STAGE % NW == 0 && IPW >= 1, "copy split");
-    static_assert(PART_BYTES <= KV_BYTES, "partials reuse the KV buffers");
+// Logical workgroup id.  The dispatcher hands workgroups to the 8 XCDs round
+// robin; the remap gives each XCD a contiguous range of logical ids, so rows
+// shared by neighbouring queries (prefill windows) or by the head groups and
+// splits of one query stay in that XCD's L2.
+__device__ __forceinline__ uint32_t logical_wg(uint32_t T) {
+    const uint32_t per = T >> 3, rem = T & 7, x = blockIdx.x & 7, k = blockIdx.x >> 3;
+    return x < rem ? x * (per + 1) + k : rem * (per + 1) + (x - rem) * per + k;
+}
+
+// Index-list compaction.  The entries of idx[c0, c1) (at most kListCap) are
+// spread over the workgroup's threads as e = c0 + k * NT + tid, k < K, and all
+// K loads of a thread are issued together, so a chunk costs one memory latency.
+// Valid entries (0 <= v < rows) are packed into list[0, nv) in (k, thread)
+// order -- deterministic, and any order is correct (each entry is independent).
+template <int NT>
+struct Compactor {
+    static constexpr int K = kListCap / NT;
+    static constexpr int NW = NT / 64;
+    int v[K];
+
+    __device__ __forceinline__ void load(const int32_t *__restrict__ idxq, int c0, int c1) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int e = c0 + k * NT + (int)threadIdx.x;
+            v[k] = e < c1 ? idxq[e] : -1;
+        }
+    }
+
+    // every thread of the workgroup calls it; returns nv
+    __device__ __forceinline__ int pack(int64_t rows, int *list, int *wcnt /* [K][NW] */) {
+        const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+        uint64_t mask[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            mask[k] = __ballot(v[k] >= 0 && (int64_t)v[k] < rows);
+            if (lane == 0) wcnt[k * NW + wave] = __popcll(mask[k]);
+        }
+        lds_barrier();
+        int base = 0;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            int pre = 0, tot = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const int cw = wcnt[k * NW + w];
+                pre += w < wave ? cw : 0;
+                tot += cw;
+            }
+            const uint64_t m = mask[k];
+            if ((m >> lane) & 1) {
+                const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+                list[base + pre + pos] = v[k];
+            }
+            base += tot;
+        }
+        lds_barrier();
+        return base;
+    }
 };
 
-template <int D, int WH, int WR>
-__global__ void __launch_bounds__(64 * WH * WR) sa_attn_kernel(const AttnParams p) {
-    using C = Cfg<D, WH, WR>;
-    __shared__ __attribute__((aligned(1024))) char smem[C::KV_BYTES];
+template <int D>
+struct WideCfg {
+    // One wavefront holds 32 heads.  Up to d = 256 it covers the whole head dim;
+    // at d = 512 its Q (128 VGPRs) and O (256 accumulators) would not fit the
+    // register file, so a pair of wavefronts splits the head dim (DH = 2) and
+    // sums its partial scores through LDS before the softmax.
+    static constexpr int DH = D > 256 ? 2 : 1;
+    static constexpr int NW = 2 * DH;            // wavefronts: 2 head tiles x DH head-dim parts
+    static constexpr int HEADS = 64;
+    static constexpr int DW = D / DH;            // head-dim slice of one wavefront
+    static constexpr int ROW_BYTES = 2 * D;
+    // LDS row stride: 3 spare 16-byte chunks per row put row r's chunk c at bank
+    // position (3 r + c) mod 16, distinct for the 16 rows of an operand fetch and
+    // for the 4 rows x 2 chunks of a transposing read -- and every operand
+    // address is a per-lane base plus a compile-time offset
+    static constexpr int RS = ROW_BYTES + 48;
+    static constexpr int CH = D / 8;             // 16-byte chunks per row
+    static constexpr int KS = DW / 16;           // k-steps of the score product
+    static constexpr int DT = DW / 32;           // 32-wide d tiles of the output
+    static constexpr int ROWS = 32;              // rows per stage
+    static constexpr int NBUF = DH > 1 ? 3 : 2;  // stage buffers: the copy runs NBUF-1 stages ahead
+    static constexpr int STAGE_BYTES = ROWS * RS;
+    static constexpr int RPW = ROWS / NW;        // rows each wavefront copies per stage
+    static constexpr int OUT_BYTES = HEADS * RS; // staged bf16 output of the workgroup
+    static constexpr int SMEM = NBUF * STAGE_BYTES > OUT_BYTES ? NBUF * STAGE_BYTES : OUT_BYTES;
+    static constexpr int XBYTES = DH > 1 ? NW * 64 * 64 : 16;  // partial-score exchange, 64 B per lane
+    static constexpr int THREADS = 64 * NW;
+    static_assert(RPW % 4 == 0 && KS >= 4 && DT >= 1, "tiling");
+};
+
+template <int D>
+__global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const AttnParams p) {
+    using C = WideCfg<D>;
+    __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
+    __shared__ __attribute__((aligned(16))) char xbuf[C::XBYTES];
     __shared__ int list[kListCap];
-    __shared__ int wcnt[C::NW];
-    __shared__ float mls[WR > 1 ? C::NW * 32 : 1];
+    __shared__ int wcnt[kListCap / 64];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
-    const int hw = wave % WH;  // head tile of this wavefront
-    const int wr = wave / WH;  // row split of this wavefront
-    const int g = lane >> 4;
-    const int n = lane & 15;
+    const int hf = lane >> 5;     // which half of a 32-wide MFMA k (or m) block this lane feeds
+    const int n = lane & 31;      // head (B / C column) or row (A row) of this lane
+    const int hw = wave / C::DH;  // head tile of this wavefront
+    const int dh = wave % C::DH;  // head-dim part of this wavefront
 
-    // Logical workgroup id: the dispatcher hands workgroups to the 8 XCDs round
-    // robin; remap so each XCD runs a contiguous range of (query, head group,
-    // split), keeping rows shared by neighbours in that XCD's L2.
-    int64_t L;
-    {
-        const int64_t T = p.total_wg, per = T >> 3, rem = T & 7;
-        const int64_t hwid = blockIdx.x, x = hwid & 7, k = hwid >> 3;
-        L = x < rem ? x * (per + 1) + k : rem * (per + 1) + (x - rem) * per + k;
-    }
-    const int sp = (int)(L % p.n_sp);
-    const int64_t t2 = L / p.n_sp;
-    const int hg = (int)(t2 % p.n_hg);
-    const int64_t qi = t2 / p.n_hg;
-    const int64_t bi = qi / p.s;
+    const uint32_t L = logical_wg((uint32_t)p.total_wg);
+    const uint32_t sp = L % (uint32_t)p.n_sp;
+    const uint32_t t2 = L / (uint32_t)p.n_sp;
+    const uint32_t hg = t2 % (uint32_t)p.n_hg;
+    const uint32_t qi = t2 / (uint32_t)p.n_hg;
+    const uint32_t bi = qi / (uint32_t)p.s;
 
-    const int head = (hg * WH + hw) * 16 + n;
+    const int lo = (int)sp * p.split_len;
+    const int hi = min(p.topk, lo + p.split_len);
+    const int32_t *idxq = p.idx + (int64_t)qi * p.topk;
+    // the first index chunk goes in flight before anything else: it heads the critical path
+    Compactor<C::THREADS> cmp;
+    cmp.load(idxq, lo, min(hi, lo + kListCap));
+
+    const int head = ((int)hg * 2 + hw) * 32 + n;
     const bool head_ok = head < p.h;
 
-    // Q as the B operand: lane (g, n) holds q[head n][32 ks + 8 g .. +8] for every ks.
+    // Q as the B operand: lane (hf, n) holds q[head n][slice + 16 ks + 8 hf .. +8] for every ks.
     bf16x8_t qreg[C::KS];
     {
-        const uint16_t *qrow = p.q + (qi * p.h + (head_ok ? head : 0)) * (int64_t)D + 8 * g;
+        const uint16_t *qrow = p.q + ((int64_t)qi * p.h + (head_ok ? head : 0)) * D + dh * C::DW + 8 * hf;
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-            if (head_ok)
-                qreg[ks] = *reinterpret_cast<const bf16x8_t *>(qrow + 32 * ks);
-            else
-                qreg[ks] = bf16x8_t{};
-        }
+        for (int ks = 0; ks < C::KS; ++ks)
+            qreg[ks] = head_ok ? *reinterpret_cast<const bf16x8_t *>(qrow + 16 * ks) : bf16x8_t{};
     }
 
-    float m_run = -1e30f;  // running max (log2 domain); finite start as in the pages' kernel
+    float m_ref = -1e30f;  // running max (log2 domain) the weights are taken against
     float l_run = 0.0f;    // this lane's share of the running sum
-    f32x4_t acc_o[C::DT];
+    f32x16_t acc_o[C::DT];
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) acc_o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < C::DT; ++dt) acc_o[dt] = f32x16_t{};
 
-    const int lo = sp * p.split_len;
-    const int hi = min(p.topk, lo + p.split_len);
-    const int32_t *idxq = p.idx + qi * (int64_t)p.topk;
-    const uint16_t *kvb = p.kv + bi * p.rows * (int64_t)D;
+    const uint16_t *kvb = p.kv + (int64_t)bi * p.rows * D;
     const uint32_t smem_base = lds_addr((const SA_LDS void *)smem);
+    const SA_LDS char *lds = (const SA_LDS char *)smem;
+    // per-lane operand bases inside a stage buffer (see the two read patterns below)
+    const int slice = 2 * dh * C::DW;  // byte offset of this wave's head-dim slice in a row
+    const int koff = n * C::RS + slice + 16 * hf;
+    const int p16 = lane & 15;
+    const int voff = (4 * hf + (p16 >> 2)) * C::RS + slice + 16 * (2 * ((lane >> 4) & 1) + ((p16 & 3) >> 1)) +
+                     ((p16 & 1) << 3);
 
     for (int c0 = lo; c0 < hi; c0 += kListCap) {
         const int c1 = min(hi, c0 + kListCap);
-        // ---- 1. compaction of idx[c0, c1) into list[0, nv) ----
-        int nv = 0;
-        for (int base = c0; base < c1; base += C::NT) {
-            const int t = base + tid;
-            const int v = t < c1 ? idxq[t] : -1;
-            const bool ok = v >= 0 && (int64_t)v < p.rows;
-            const uint64_t mask = __ballot(ok);
-            const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
-            if (lane == 0) wcnt[wave] = __popcll(mask);
-            __syncthreads();
-            int pre = 0, tot = 0;
-#pragma unroll
-            for (int w = 0; w < C::NW; ++w) {
-                const int cw = wcnt[w];
-                pre += w < wave ? cw : 0;
-                tot += cw;
-            }
-            if (ok) list[nv + pre + pos] = v;
-            nv += tot;
-            __syncthreads();
-        }
+        if (c0 != lo) cmp.load(idxq, c0, c1);
+        const int nv = cmp.pack(p.rows, list, wcnt);
         if (nv == 0) continue;
+        const int nst = (nv + C::ROWS - 1) / C::ROWS;
+        const int last_row = list[nv - 1];
 
-        // ---- 2. gather pipeline ----
-        const int nst = (nv + C::ROWS_STAGE - 1) / C::ROWS_STAGE;
+        // copies of one stage: this wave's RPW rows, one wave instruction (one row) each;
+        // the list entries are read in one go, entries past the end repeat the last valid row
         auto issue = [&](int st) {
             const uint32_t buf = smem_base + (uint32_t)((st % C::NBUF) * C::STAGE_BYTES);
+            const int e0 = st * C::ROWS + wave * C::RPW;
+            int rowv[C::RPW];
 #pragma unroll
-            for (int u = 0; u < C::IPW; ++u) {
-                const int inst = wave * C::IPW + u;
-                const int r = inst * C::RPI + lane / C::CH;  // row within the stage
-                const int e = min(st * C::ROWS_STAGE + r, nv - 1);  // past the end: repeat a valid row
-                const int row = list[e];
-                const int chunk = (lane % C::CH) ^ swz<D>(r);
-                const uint16_t *src = kvb + (int64_t)row * D + chunk * 8;
-                dma_16B(src, __builtin_amdgcn_readfirstlane(buf + inst * 1024));
+            for (int u = 0; u < C::RPW; u += 4) {
+                const i32x4_t r4 = *reinterpret_cast<const SA_LDS i32x4_t *>((const SA_LDS int *)list + e0 + u);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) rowv[u + c] = e0 + u + c < nv ? r4[c] : last_row;
+            }
+#pragma unroll
+            for (int u = 0; u < C::RPW; ++u) {
+                const int r = wave * C::RPW + u;
+                if (C::CH == 64 || lane < C::CH)
+                    dma_16B(kvb + (int64_t)rowv[u] * D + lane * 8, __builtin_amdgcn_readfirstlane(buf + r * C::RS));
             }
         };
 
         issue(0);
+        if (C::NBUF > 2 && nst > 1) issue(1);
         for (int st = 0; st < nst; ++st) {
-            if (C::NBUF == 2 && st + 1 < nst) {
-                issue(st + 1);
-                wait_vmcnt_barrier<C::IPW>();
+            if (st + C::NBUF - 1 < nst) {
+                issue(st + C::NBUF - 1);
+                wait_vmcnt_barrier<(C::NBUF - 1) * C::RPW>();
+            } else if (C::NBUF > 2 && st + 1 < nst) {
+                wait_vmcnt_barrier<C::RPW>();
             } else {
                 wait_vmcnt_barrier<0>();
             }
-            const SA_LDS char *buf = (const SA_LDS char *)smem +
-                                     (st % C::NBUF) * C::STAGE_BYTES + wr * kBlk * C::ROW_BYTES;
-            const int ebase = st * C::ROWS_STAGE + wr * kBlk;
+            const SA_LDS char *buf = lds + (st % C::NBUF) * C::STAGE_BYTES;
 
-            // ---- 3. scores S^T for this wave's 32 rows x 16 heads ----
-            f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+            // ---- 3. scores: lane (hf, n) feeds row n, d chunk 2 ks + hf.  Operand reads
+            //      run four MFMAs ahead; the scheduling barriers keep the compiler from
+            //      hoisting all of them (which would spill the accumulators) ----
+            f32x16_t sacc = {};
             {
-                const int ra0 = rho(n), ra1 = 16 + rho(n);
-                const SA_LDS char *p0 = buf + ra0 * C::ROW_BYTES;
-                const SA_LDS char *p1 = buf + ra1 * C::ROW_BYTES;
-                const int z0 = swz<D>(ra0), z1 = swz<D>(ra1);
+                const SA_LDS char *kb = buf + koff;
+                constexpr int PF = 4;
+                bf16x8_t kq[PF];
+#pragma unroll
+                for (int i = 0; i < PF; ++i) kq[i] = lds_read_b128(kb + 32 * i);
 #pragma unroll
                 for (int ks = 0; ks < C::KS; ++ks) {
-                    const int c = 4 * ks + g;
-                    const bf16x8_t a0 = lds_read_b128(p0 + ((c ^ z0) << 4));
-                    const bf16x8_t a1 = lds_read_b128(p1 + ((c ^ z1) << 4));
-                    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qreg[ks], s0, 0, 0, 0);
-                    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qreg[ks], s1, 0, 0, 0);
+                    const bf16x8_t a = kq[ks % PF];
+                    if (ks + PF < C::KS) kq[ks % PF] = lds_read_b128(kb + 32 * (ks + PF));
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc, 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
 
-            // ---- 4. online softmax (lane column = head n; rows rho(4g+i)) ----
-            float sc[8];
+            if (C::DH > 1) {
+                // the pair's partial scores over its two head-dim halves: each wave adds
+                // the other's, so both hold the same full-dim sums (f32 addition commutes)
+                SA_LDS char *xb = (SA_LDS char *)xbuf;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = rho(4 * g + i);
-                sc[i] = ebase + r < nv ? s0[i] * p.scale_log2 : -INFINITY;
-                sc[4 + i] = ebase + 16 + r < nv ? s1[i] * p.scale_log2 : -INFINITY;
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<SA_LDS f32x4_t *>(xb + ((wave * 4 + j) * 64 + lane) * 16) =
+                        f32x4_t{sacc[4 * j], sacc[4 * j + 1], sacc[4 * j + 2], sacc[4 * j + 3]};
+                lds_barrier();
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f32x4_t o =
+                        *reinterpret_cast<const SA_LDS f32x4_t *>(xb + (((wave ^ 1) * 4 + j) * 64 + lane) * 16);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sacc[4 * j + e] += o[e];
+                }
             }
-            float mx = sc[0];
+
+            // ---- 4. softmax: value i of lane (hf, n) is row 8(i/4) + 4 hf + i%4, head n ----
+            const int ebase = st * C::ROWS;
+            float sv[16];
+            float mx = -INFINITY;
+            if (ebase + C::ROWS <= nv) {
 #pragma unroll
-            for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
-            mx = fmaxf(mx, shfl_xor_f32(mx, 16));
+                for (int i = 0; i < 16; ++i) {
+                    sv[i] = sacc[i] * p.scale_log2;
+                    mx = fmaxf(mx, sv[i]);
+                }
+            } else {  // last, partial stage: rows past the list end weigh nothing
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int r = 8 * (i >> 2) + 4 * hf + (i & 3);
+                    sv[i] = ebase + r < nv ? sacc[i] * p.scale_log2 : -INFINITY;
+                    mx = fmaxf(mx, sv[i]);
+                }
+            }
             mx = fmaxf(mx, shfl_xor_f32(mx, 32));
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = exp2_fast(m_run - m_new);
-            uint32_t pk[4];
-            float psum = 0.f;
+            if (__ballot(mx > m_ref + kRescaleSlack)) {
+                const float m_new = fmaxf(m_ref, mx);
+                if (__ballot(m_ref > -1e29f)) {
+                    const float alpha = exp2_fast(m_ref - m_new);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t bits = pack_bf16x2(exp2_fast(sc[2 * i] - m_new),
-                                                  exp2_fast(sc[2 * i + 1] - m_new));
-                pk[i] = bits;
-                psum += __uint_as_float(bits << 16) + __uint_as_float(bits & 0xffff0000u);
+                    for (int dt = 0; dt < C::DT; ++dt) acc_o[dt] *= alpha;
+                    l_run *= alpha;
+                }
+                m_ref = m_new;
             }
-            l_run = l_run * alpha + psum;
-            m_run = m_new;
-            if (__ballot(alpha != 1.0f)) {
+            uint32_t pk[8];
 #pragma unroll
-                for (int dt = 0; dt < C::DT; ++dt) acc_o[dt] *= alpha;
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t b = pack_bf16x2(exp2_fast(sv[2 * i] - m_ref), exp2_fast(sv[2 * i + 1] - m_ref));
+                pk[i] = b;
+                l_run += __uint_as_float(b << 16) + __uint_as_float(b & 0xffff0000u);
             }
-            bf16x8_t pb;
-            {
-                u32x4_t pw = {pk[0], pk[1], pk[2], pk[3]};
-                pb = __builtin_bit_cast(bf16x8_t, pw);
-            }
+            const bf16x8_t pb0 = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
+            const bf16x8_t pb1 = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[4], pk[5], pk[6], pk[7]});
 
-            // ---- 5. O^T += V^T P^T ----
+            // ---- 5. O^T += V^T P^T.  MFMA j = kk DT + dt; for it, the 16-lane group
+            //      (hf, column half) reads rows 16 kk + 8 rd + 4 hf + p/4 (rd = 0, 1),
+            //      columns 32 dt + 16 (column half) + 4 (p%4), p = lane % 16 ----
             {
-                const int rr0 = rho(4 * g + (n >> 2)), rr1 = 16 + rr0;
-                const SA_LDS char *p0 = buf + rr0 * C::ROW_BYTES + ((n & 1) << 3);
-                const SA_LDS char *p1 = buf + rr1 * C::ROW_BYTES + ((n & 1) << 3);
-                const int z0 = swz<D>(rr0), z1 = swz<D>(rr1);
-                const int csub = (n & 3) >> 1;
+                const SA_LDS char *vb = buf + voff;
+                auto vread = [&](int j) {
+                    const int dt = j % C::DT, kk = j / C::DT;
+                    const i16x4_t lo4 = lds_read_tr16(vb + (16 * kk) * C::RS + 64 * dt);
+                    const i16x4_t hi4 = lds_read_tr16(vb + (16 * kk + 8) * C::RS + 64 * dt);
+                    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+                };
+                constexpr int NJ = 2 * C::DT;
+                constexpr int PF = 3;
+                bf16x8_t vq[PF];
 #pragma unroll
-                for (int dt = 0; dt < C::DT; ++dt) {
-                    const int c = 2 * dt + csub;
-                    const i16x4_t lo4 = lds_read_tr16(p0 + ((c ^ z0) << 4));
-                    const i16x4_t hi4 = lds_read_tr16(p1 + ((c ^ z1) << 4));
-                    const bf16x8_t a = __builtin_bit_cast(
-                        bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-                    acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, acc_o[dt], 0, 0, 0);
+                for (int i = 0; i < PF; ++i) vq[i] = vread(i);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const bf16x8_t a = vq[j % PF];
+                    if (j + PF < NJ) vq[j % PF] = vread(j + PF);
+                    acc_o[j % C::DT] =
+                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, j >= C::DT ? pb1 : pb0, acc_o[j % C::DT], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            lds_barrier();  // every wave is done with this buffer
-            if (C::NBUF == 1 && st + 1 < nst) issue(st + 1);
+            lds_barrier();  // every wave is done with this buffer and the exchange slots
         }
     }
 
-    // full running sum of the head: add the shares of the four lane groups
-    l_run += shfl_xor_f32(l_run, 16);
+    // full running sum of the head: add the other half's share
     l_run += shfl_xor_f32(l_run, 32);
 
     if (p.n_sp > 1) {
         // ---- 6b. split partials: unnormalised O, running max and sum, no sink ----
         if (head_ok) {
-            const int64_t prow = (qi * p.n_sp + sp) * p.h + head;
-            float *po = p.part_o + prow * D + 4 * g;
+            const int64_t prow = ((int64_t)qi * p.n_sp + sp) * p.h + head;
+            float *po = p.part_o + prow * D + dh * C::DW + 4 * hf;
 #pragma unroll
-            for (int dt = 0; dt < C::DT; ++dt) *reinterpret_cast<f32x4_t *>(po + 16 * dt) = acc_o[dt];
-            if (g == 0) {
-                p.part_ml[prow * 2] = m_run;
+            for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+                for (int qd = 0; qd < 4; ++qd)
+                    *reinterpret_cast<f32x4_t *>(po + 32 * dt + 8 * qd) =
+                        f32x4_t{acc_o[dt][4 * qd], acc_o[dt][4 * qd + 1], acc_o[dt][4 * qd + 2],
+                                acc_o[dt][4 * qd + 3]};
+            if (hf == 0 && dh == 0) {
+                p.part_ml[prow * 2] = m_ref;
                 p.part_ml[prow * 2 + 1] = l_run;
             }
         }
         return;
     }
 
-    const float sink_l2 = head_ok ? p.sink[head] * kLog2e : 0.f;
-    uint16_t *orow = p.out + (qi * p.h + (head_ok ? head : 0)) * (int64_t)D + 4 * g;
-
-    if (WR == 1) {
-        // ---- 6. sink fold + normalise + store ----
-        if (!head_ok) return;
-        const float Lt = l_run + exp2_fast(sink_l2 - m_run);
-        const float inv = Lt > 0.f ? 1.0f / Lt : 0.f;  // empty list: 0 / inf or guarded 0 / 0
+    // ---- 6. sink fold + normalise, stage bf16 rows in LDS, store a row per instruction ----
+    {
+        const float sink_l2 = head_ok ? p.sink[head] * kLog2e : 0.f;
+        const float Lt = l_run + exp2_fast(sink_l2 - m_ref);
+        const float inv = Lt > 0.f ? 1.0f / Lt : 0.f;  // empty list: 0 / inf, or a guarded 0 / 0
+        // lane (hf, n) holds head n, d = 32 dt + 8 qd + 4 hf + (0..3)
+        SA_LDS char *orow = (SA_LDS char *)smem + (hw * 32 + n) * C::RS + slice + 8 * hf;
 #pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt) {
-            const f32x4_t o = acc_o[dt] * inv;
-            u32x2_t w = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-            *reinterpret_cast<u32x2_t *>(orow + 16 * dt) = w;
+        for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                const u32x2_t w = {pack_bf16x2(acc_o[dt][4 * qd] * inv, acc_o[dt][4 * qd + 1] * inv),
+                                   pack_bf16x2(acc_o[dt][4 * qd + 2] * inv, acc_o[dt][4 * qd + 3] * inv)};
+                *reinterpret_cast<SA_LDS u32x2_t *>(orow + 64 * dt + 16 * qd) = w;
+            }
+    }
+    lds_barrier();
+    // one head row per wave instruction: lane l stores chunk l (16 B) of the row
+#pragma unroll 4
+    for (int hr = wave; hr < C::HEADS; hr += C::NW) {
+        const int hglob = (int)hg * C::HEADS + hr;
+        if (hglob < p.h && (C::CH == 64 || lane < C::CH)) {
+            const u32x4_t v = *reinterpret_cast<const SA_LDS u32x4_t *>(lds + hr * C::RS + 16 * lane);
+            *reinterpret_cast<u32x4_t *>(p.out + ((int64_t)qi * p.h + hglob) * D + lane * 8) = v;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ decode --
+//
+// Decode kernel: one workgroup of four wavefronts per (query, group of 16
+// heads), for short index lists.  A stage holds up to 128 gathered rows; the
+// four wavefronts split the rows for the scores (S^T[32 rows][16 heads] each,
+// MFMA 16x16x32), exchange the per-head maxima and the bf16 weights P through
+// LDS, then split the head dim for O^T[128 d][16 heads] = V^T P^T over all the
+// stage's rows.  Every gathered row is read from LDS once as K and once as V,
+// and no partial result leaves the workgroup.
+template <int D>
+struct DecodeCfg {
+    static constexpr int NW = 4;
+    static constexpr int THREADS = 64 * NW;
+    static constexpr int ROWS = 32 * NW;          // rows per stage
+    static constexpr int ROW_BYTES = 2 * D;
+    static constexpr int RS = ROW_BYTES + 48;     // padded LDS row stride (bank position 3 r + c)
+    static constexpr int CH = D / 8;
+    static constexpr int KS = D / 32;             // k-steps of the score product (16x16x32)
+    static constexpr int DQ = D / NW;             // head-dim share of one wavefront in the weighted sum
+    static constexpr int DT = DQ / 16;            // its 16-wide d tiles
+    static constexpr int RPW = ROWS / NW;         // rows each wavefront copies per stage
+    static constexpr int PRS = 2 * ROWS + 16;     // padded row stride of the weight buffer P[head][row]
+    static constexpr int STAGE_BYTES = ROWS * RS;
+    static_assert(KS >= 2 && DT >= 1 && RPW % 4 == 0, "tiling");
+};
+
+template <int D>
+__global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
+    using C = DecodeCfg<D>;
+    __shared__ __attribute__((aligned(1024))) char smem[C::STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) char pbuf[16 * C::PRS];
+    __shared__ float smax[C::NW][16];
+    __shared__ float ssum[C::NW][16];
+    __shared__ int list[kListCap];
+    __shared__ int wcnt[kListCap / 64];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int g = lane >> 4;  // 16-lane group: k (or m) block of a 16x16x32 operand
+    const int n = lane & 15;  // head (B / C column) or row (A row)
+
+    const uint32_t L = logical_wg((uint32_t)p.total_wg);
+    const uint32_t sp = L % (uint32_t)p.n_sp;
+    const uint32_t t2 = L / (uint32_t)p.n_sp;
+    const uint32_t hg = t2 % (uint32_t)p.n_hg;
+    const uint32_t qi = t2 / (uint32_t)p.n_hg;
+    const uint32_t bi = qi / (uint32_t)p.s;
+
+    const int lo = (int)sp * p.split_len;
+    const int hi = min(p.topk, lo + p.split_len);
+    const int32_t *idxq = p.idx + (int64_t)qi * p.topk;
+    Compactor<C::THREADS> cmp;
+    cmp.load(idxq, lo, min(hi, lo + kListCap));
+
+    const int head = (int)hg * 16 + n;
+    const bool head_ok = head < p.h;
+    // Q as the B operand of the scores: lane (g, n) holds q[head n][32 ks + 8 g .. +8]
+    bf16x8_t qreg[C::KS];
+    {
+        const uint16_t *qrow = p.q + ((int64_t)qi * p.h + (head_ok ? head : 0)) * D + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks)
+            qreg[ks] = head_ok ? *reinterpret_cast<const bf16x8_t *>(qrow + 32 * ks) : bf16x8_t{};
+    }
+
+    float m_ref = -1e30f;  // reference max (log2 domain), identical in all four wavefronts
+    float l_run = 0.0f;    // this lane's share of the running sum over this wave's rows
+    f32x4_t acc_o[C::DT];
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) acc_o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const uint16_t *kvb = p.kv + (int64_t)bi * p.rows * D;
+    const uint32_t smem_base = lds_addr((const SA_LDS void *)smem);
+    const SA_LDS char *lds = (const SA_LDS char *)smem;
+    const SA_LDS char *pl = (const SA_LDS char *)pbuf;
+    // score operand: row 32 wave + 16 t + n, d chunk 4 ks + g
+    const SA_LDS char *kb = lds + (32 * wave + n) * C::RS + 16 * g;
+    // weighted-sum operand (transposing read): rows 32 ks + 8 g + 4 rd + p/4, d 16 dt + 4 (p%4) of this wave's quarter
+    const SA_LDS char *vb = lds + (8 * g + (n >> 2)) * C::RS + 2 * C::DQ * wave + 8 * (n & 3);
+
+    for (int c0 = lo; c0 < hi; c0 += kListCap) {
+        const int c1 = min(hi, c0 + kListCap);
+        if (c0 != lo) cmp.load(idxq, c0, c1);
+        const int nv = cmp.pack(p.rows, list, wcnt);
+        if (nv == 0) continue;
+        const int last_row = list[nv - 1];
+        for (int ebase = 0; ebase < nv; ebase += C::ROWS) {
+            // ---- gather this stage: each wave copies 32 rows, one row per instruction ----
+            {
+                const int e0 = ebase + wave * C::RPW;
+                int rowv[C::RPW];
+#pragma unroll
+                for (int u = 0; u < C::RPW; u += 4) {
+                    const i32x4_t r4 = *reinterpret_cast<const SA_LDS i32x4_t *>((const SA_LDS int *)list + e0 + u);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) rowv[u + c] = e0 + u + c < nv ? r4[c] : last_row;
+                }
+#pragma unroll
+                for (int u = 0; u < C::RPW; ++u)
+                    if (C::CH == 64 || lane < C::CH)
+                        dma_16B(kvb + (int64_t)rowv[u] * D + lane * 8,
+                                __builtin_amdgcn_readfirstlane(smem_base + (wave * C::RPW + u) * C::RS));
+                wait_vmcnt_barrier<0>();
+            }
+
+            // ---- scores S^T for this wave's 32 rows: two 16-row tiles ----
+            f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ++ks) {
+                const bf16x8_t a0 = lds_read_b128(kb + 64 * ks);
+                const bf16x8_t a1 = lds_read_b128(kb + 16 * C::RS + 64 * ks);
+                s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qreg[ks], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qreg[ks], s1, 0, 0, 0);
+            }
+            // value i of tile t in lane (g, n): row 32 wave + 16 t + 4 g + i, head n
+            float sv[8];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = ebase + 32 * wave + 4 * g + i;
+                sv[i] = r < nv ? s0[i] * p.scale_log2 : -INFINITY;
+                sv[4 + i] = r + 16 < nv ? s1[i] * p.scale_log2 : -INFINITY;
+                mx = fmaxf(mx, fmaxf(sv[i], sv[4 + i]));
+            }
+            mx = fmaxf(mx, shfl_xor_f32(mx, 16));
+            mx = fmaxf(mx, shfl_xor_f32(mx, 32));
+            if (g == 0) smax[wave][n] = mx;
+            lds_barrier();
+            float ms = fmaxf(fmaxf(smax[0][n], smax[1][n]), fmaxf(smax[2][n], smax[3][n]));
+            if (__ballot(ms > m_ref + kRescaleSlack)) {  // same decision in every wave
+                const float m_new = fmaxf(m_ref, ms);
+                if (__ballot(m_ref > -1e29f)) {
+                    const float alpha = exp2_fast(m_ref - m_new);
+#pragma unroll
+                    for (int dt = 0; dt < C::DT; ++dt) acc_o[dt] *= alpha;
+                    l_run *= alpha;
+                }
+                m_ref = m_new;
+            }
+            // weights -> bf16 -> P[head][row] in LDS (rows 32 wave + 16 t + 4 g + 0..3)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const uint32_t b0 = pack_bf16x2(exp2_fast(sv[4 * t] - m_ref), exp2_fast(sv[4 * t + 1] - m_ref));
+                const uint32_t b1 = pack_bf16x2(exp2_fast(sv[4 * t + 2] - m_ref), exp2_fast(sv[4 * t + 3] - m_ref));
+                l_run += __uint_as_float(b0 << 16) + __uint_as_float(b0 & 0xffff0000u) +
+                         __uint_as_float(b1 << 16) + __uint_as_float(b1 & 0xffff0000u);
+                *reinterpret_cast<SA_LDS u32x2_t *>((SA_LDS char *)pl + n * C::PRS + 2 * (32 * wave + 16 * t + 4 * g)) =
+                    u32x2_t{b0, b1};
+            }
+            lds_barrier();
+
+            // ---- O^T[this wave's d quarter][16 heads] += V^T P^T over the stage's rows ----
+            const int nks = min(C::ROWS, nv - ebase + 31) / 32;  // 32-row k-steps holding data
+#pragma unroll
+            for (int ks = 0; ks < C::ROWS / 32; ++ks) {
+                if (ks < nks) {
+                    const bf16x8_t pb = lds_read_b128(pl + n * C::PRS + 2 * (32 * ks + 8 * g));
+#pragma unroll
+                    for (int dt = 0; dt < C::DT; ++dt) {
+                        const i16x4_t lo4 = lds_read_tr16(vb + (32 * ks) * C::RS + 32 * dt);
+                        const i16x4_t hi4 = lds_read_tr16(vb + (32 * ks + 4) * C::RS + 32 * dt);
+                        const bf16x8_t a =
+                            __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+                        acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, acc_o[dt], 0, 0, 0);
+                    }
+                }
+            }
+            lds_barrier();  // buffer and weights free for the next stage
+        }
+    }
+
+    // this wave's share of the sum: add the four lane groups, then the four waves
+    l_run += shfl_xor_f32(l_run, 16);
+    l_run += shfl_xor_f32(l_run, 32);
+    if (g == 0) ssum[wave][n] = l_run;
+    lds_barrier();
+    const float l_tot = (ssum[0][n] + ssum[1][n]) + (ssum[2][n] + ssum[3][n]);
+
+    if (p.n_sp > 1) {
+        if (head_ok) {
+            const int64_t prow = ((int64_t)qi * p.n_sp + sp) * p.h + head;
+            float *po = p.part_o + prow * D + C::DQ * wave + 4 * g;
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt) *reinterpret_cast<f32x4_t *>(po + 16 * dt) = acc_o[dt];
+            if (wave == 0 && g == 0) {
+                p.part_ml[prow * 2] = m_ref;
+                p.part_ml[prow * 2 + 1] = l_tot;
+            }
         }
         return;
     }
-
-    // ---- 6c. in-workgroup combine of the WR row-split waves of each head tile ----
-    {
-        float *part = reinterpret_cast<float *>(smem);
-        const int slot = hw * WR + wr;
+    if (!head_ok) return;
+    const float Lt = l_tot + exp2_fast(p.sink[head] * kLog2e - m_ref);
+    const float inv = Lt > 0.f ? 1.0f / Lt : 0.f;
+    // lane (g, n) holds head n, d = quarter + 16 dt + 4 g + (0..3)
+    uint16_t *orow = p.out + ((int64_t)qi * p.h + head) * D + C::DQ * wave + 4 * g;
 #pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt)
-            *reinterpret_cast<f32x4_t *>(part + ((slot * C::DT + dt) * 64 + lane) * 4) = acc_o[dt];
-        if (g == 0) {
-            mls[(slot * 16 + n) * 2] = m_run;
-            mls[(slot * 16 + n) * 2 + 1] = l_run;
-        }
-        lds_barrier();
-        float mr[WR], wgt[WR];
-        float M = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < WR; ++r) {
-            mr[r] = mls[((hw * WR + r) * 16 + n) * 2];
-            M = fmaxf(M, mr[r]);
-        }
-        float Lt = 0.f;
-#pragma unroll
-        for (int r = 0; r < WR; ++r) {
-            wgt[r] = exp2_fast(mr[r] - M);
-            Lt += mls[((hw * WR + r) * 16 + n) * 2 + 1] * wgt[r];
-        }
-        Lt += exp2_fast(sink_l2 - M);
-        const float inv = Lt > 0.f ? 1.0f / Lt : 0.f;
-        if (!head_ok) return;
-        constexpr int DPW = C::DT / WR;  // d tiles finalised by each row-split wave
-#pragma unroll
-        for (int j = 0; j < DPW; ++j) {
-            const int dt = wr * DPW + j;
-            f32x4_t o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int r = 0; r < WR; ++r)
-                o += *reinterpret_cast<const f32x4_t *>(part + (((hw * WR + r) * C::DT + dt) * 64 + lane) * 4) *
-                     wgt[r];
-            o *= inv;
-            u32x2_t w = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-            *reinterpret_cast<u32x2_t *>(orow + 16 * dt) = w;
-        }
+    for (int dt = 0; dt < C::DT; ++dt) {
+        const f32x4_t o = acc_o[dt] * inv;
+        *reinterpret_cast<u32x2_t *>(orow + 16 * dt) = u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
     }
 }
 
@@ -414,7 +674,10 @@ __global__ void __launch_bounds__(256) sa_combine_kernel(const float *__restrict
 // ------------------------------------------------------------------ dispatch --
 
 struct Variant {
-    int wh, wr, n_sp, split_len;
+    int kernel;     // SA_KERNEL_WIDE or SA_KERNEL_DECODE
+    int heads_wg;   // heads per workgroup
+    int n_sp;       // index splits across workgroups
+    int split_len;  // entries per split
 };
 
 int cu_count() {
@@ -425,35 +688,34 @@ int cu_count() {
     return cus;
 }
 
-// Chooses the variant from the problem shape and the CU count.
-//  - heads are tiled 16 per wavefront; a workgroup takes up to 4 head tiles;
-//  - with too few (query, head group) workgroups to fill the chip, heads are
-//    split into single-tile groups whose four wavefronts split the index list
-//    and combine in LDS (rows are shared through L2 between the groups of one
-//    query), and only then is the list split across workgroups with an f32
-//    combine pass.
+void set_splits(Variant &v, int32_t topk, int n_sp) {
+    n_sp = std::max(1, n_sp);
+    int len = (std::max(topk, 1) + n_sp - 1) / n_sp;
+    len = (len + 31) / 32 * 32;  // whole 32-row stages per split
+    v.split_len = len;
+    v.n_sp = std::max(1, (topk + len - 1) / len);
+}
+
+// Automatic choice from the problem shape and the CU count (thresholds from
+// measurements on MI355X).  Short lists in decode-sized batches (fewer
+// (query, 64-head group) pairs than two per CU) go to the decode kernel on
+// 16-head groups; everything else to the wide kernel.  The index list is split
+// across workgroups (f32 combine pass) only when the chosen kernel would leave
+// CUs idle and the list is long enough to share.
+constexpr int kDecodeMaxTopk = 512;
+
 Variant choose_variant(int64_t nq, int32_t h, int32_t topk, int cus) {
-    const int n_ht = (h + 15) / 16;
-    Variant v{std::min(4, n_ht), 1, 1, std::max(topk, 1)};
-    const int64_t target = 2LL * cus;
-    int64_t wgs = nq * ((n_ht + v.wh - 1) / v.wh);
-    if (wgs >= target) return v;
-    if (topk > 2 * kBlk) {
-        // spread heads over more workgroups, filling each with row-split waves
-        v.wh = 1;
-        v.wr = 4;
-        wgs = nq * n_ht;
-        if (wgs >= cus) return v;
-        // still too few: split the list across workgroups as well
-        v.wr = 1;
-        v.wh = std::min(4, n_ht);
-        wgs = nq * ((n_ht + v.wh - 1) / v.wh);
-        int n_sp = (int)std::min<int64_t>((target + wgs - 1) / wgs, (topk + 127) / 128);
-        n_sp = std::max(1, std::min(n_sp, 64));
-        v.n_sp = n_sp;
-        v.split_len = (topk + n_sp - 1) / n_sp;
-        v.split_len = (v.split_len + kBlk - 1) / kBlk * kBlk;
-        v.n_sp = (topk + v.split_len - 1) / v.split_len;
+    Variant v{SA_KERNEL_WIDE, 64, 1, std::max(topk, 1)};
+    const int64_t wide_wgs = nq * ((h + 63) / 64);
+    if (wide_wgs < 2LL * cus && topk <= kDecodeMaxTopk) {
+        v.kernel = SA_KERNEL_DECODE;
+        v.heads_wg = 16;
+    }
+    const int64_t wgs = nq * ((h + v.heads_wg - 1) / v.heads_wg);
+    const int min_len = v.kernel == SA_KERNEL_DECODE ? 128 : 256;
+    if (wgs < cus && topk >= 2 * min_len) {
+        const int64_t want = (cus + wgs - 1) / wgs;
+        set_splits(v, topk, (int)std::min<int64_t>(want, topk / min_len));
     }
     return v;
 }
@@ -463,77 +725,60 @@ size_t workspace_for(const Variant &v, int64_t nq, int32_t h, int32_t d) {
     return (size_t)nq * v.n_sp * h * ((size_t)d + 2) * sizeof(float);
 }
 
-template <int D, int WH, int WR>
-hipError_t launch_attn(const AttnParams &p, hipStream_t stream) {
-    hipLaunchKernelGGL((sa_attn_kernel<D, WH, WR>), dim3((unsigned)p.total_wg), dim3(64 * WH * WR), 0,
-                       stream, p);
+sa_status resolve_variant(int64_t nq, int32_t h, int32_t topk, int32_t kernel, int32_t splits, Variant *out) {
+    Variant v = choose_variant(nq, h, topk, cu_count());
+    if (kernel != 0 && kernel != SA_KERNEL_WIDE && kernel != SA_KERNEL_DECODE) return SA_ERR_UNSUPPORTED;
+    if (splits < 0) return SA_ERR_UNSUPPORTED;
+    if (kernel != 0 && kernel != v.kernel) {
+        v.kernel = kernel;
+        v.heads_wg = kernel == SA_KERNEL_WIDE ? 64 : 16;
+        set_splits(v, topk, 1);
+    }
+    if (splits > 0) set_splits(v, topk, splits);
+    *out = v;
+    return SA_OK;
+}
+
+template <int D>
+hipError_t launch_wide(const AttnParams &p, hipStream_t stream) {
+    hipLaunchKernelGGL((sa_attn_wide<D>), dim3((unsigned)p.total_wg), dim3(WideCfg<D>::THREADS), 0, stream, p);
     return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(const AttnParams &p, int wh, int wr, hipStream_t stream) {
-    if (wr == 1) {
-        if (wh == 1) return launch_attn<D, 1, 1>(p, stream);
-        if (wh == 2) return launch_attn<D, 2, 1>(p, stream);
-        return launch_attn<D, 4, 1>(p, stream);
-    }
-    if (wr == 2) {
-        if (wh == 1) return launch_attn<D, 1, 2>(p, stream);
-        return launch_attn<D, 2, 2>(p, stream);
-    }
-    return launch_attn<D, 1, 4>(p, stream);
+hipError_t launch_decode(const AttnParams &p, hipStream_t stream) {
+    hipLaunchKernelGGL((sa_attn_decode<D>), dim3((unsigned)p.total_wg), dim3(DecodeCfg<D>::THREADS), 0, stream, p);
+    return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_combine(const AttnParams &p, hipStream_t stream) {
-    const int64_t n = p.nq * p.h * (D / 8);
+    const int64_t n = (int64_t)p.nq * p.h * (D / 8);
     hipLaunchKernelGGL((sa_combine_kernel<D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                       p.part_o, p.part_ml, p.sink, p.out, p.nq, p.h, p.n_sp);
+                       p.part_o, p.part_ml, p.sink, p.out, (int64_t)p.nq, p.h, p.n_sp);
     return hipGetLastError();
 }
 
 bool valid_d(int32_t d) { return d == 64 || d == 128 || d == 256 || d == 512; }
 
-sa_status resolve_variant(int64_t nq, int32_t h, int32_t topk, int32_t heads_per_wg, int32_t row_waves,
-                          int32_t splits, Variant *out) {
-    Variant v = choose_variant(nq, h, topk, cu_count());
-    if (heads_per_wg || row_waves || splits) {
-        const int wh = heads_per_wg ? heads_per_wg / 16 : v.wh;
-        const int wr = row_waves ? row_waves : (heads_per_wg ? 1 : v.wr);
-        const int sp = splits ? splits : 1;
-        if (heads_per_wg && heads_per_wg != 16 && heads_per_wg != 32 && heads_per_wg != 64)
-            return SA_ERR_UNSUPPORTED;
-        if (wr != 1 && wr != 2 && wr != 4) return SA_ERR_UNSUPPORTED;
-        if (wh * wr > 4 || (wr == 2 && wh > 2) || (wr == 4 && wh > 1)) return SA_ERR_UNSUPPORTED;
-        if (sp < 1 || (sp > 1 && wr != 1)) return SA_ERR_UNSUPPORTED;
-        v.wh = wh;
-        v.wr = wr;
-        v.n_sp = sp;
-        v.split_len = std::max(1, (topk + sp - 1) / sp);
-        if (sp > 1) v.n_sp = std::max(1, (topk + v.split_len - 1) / v.split_len);
-    }
-    *out = v;
-    return SA_OK;
-}
-
 sa_status run_sparse_attn(const uint16_t *q, const uint16_t *kv, const float *sink, const int32_t *idx,
                           int64_t b, int64_t s, int32_t h, int32_t d, int64_t rows, int32_t topk,
                           float scale, uint16_t *out, void *workspace, size_t workspace_bytes,
-                          void *stream, int32_t heads_per_wg, int32_t row_waves, int32_t splits) {
+                          void *stream, int32_t kernel, int32_t splits) {
     if (b < 0 || s < 0 || h < 0 || d < 0 || rows < 0 || topk < 0) return SA_ERR_SHAPE;
     if (!valid_d(d)) return SA_ERR_UNSUPPORTED;
     const int64_t nq = b * s;
     if (nq == 0 || h == 0) return SA_OK;
     if (!q || !sink || !out || (topk > 0 && !idx) || (rows > 0 && !kv)) return SA_ERR_NULL;
-    if (rows > 0x7fffffffLL) return SA_ERR_SHAPE;  // int32 indices
+    if (rows > 0x7fffffffLL || nq > 0x7fffffffLL) return SA_ERR_SHAPE;
     if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(kv) | reinterpret_cast<uintptr_t>(out)) % 16)
         return SA_ERR_SHAPE;
     Variant v;
-    sa_status st = resolve_variant(nq, h, topk, heads_per_wg, row_waves, splits, &v);
+    sa_status st = resolve_variant(nq, h, topk, kernel, splits, &v);
     if (st != SA_OK) return st;
     const size_t need = workspace_for(v, nq, h, d);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return SA_ERR_SHAPE;
-    const int n_ht = (h + 15) / 16;
+    if (need > 0 && (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 16))
+        return SA_ERR_SHAPE;
     AttnParams p;
     p.q = q;
     p.kv = kv;
@@ -542,24 +787,34 @@ sa_status run_sparse_attn(const uint16_t *q, const uint16_t *kv, const float *si
     p.out = out;
     p.part_o = need ? reinterpret_cast<float *>(workspace) : nullptr;
     p.part_ml = need ? reinterpret_cast<float *>(workspace) + (size_t)nq * v.n_sp * h * d : nullptr;
-    p.nq = nq;
-    p.s = s;
     p.rows = rows;
+    p.nq = (int32_t)nq;
+    p.s = (int32_t)s;
     p.h = h;
     p.topk = topk;
-    p.n_hg = (n_ht + v.wh - 1) / v.wh;
+    p.n_hg = (h + v.heads_wg - 1) / v.heads_wg;
     p.n_sp = v.n_sp;
     p.split_len = v.split_len;
     p.scale_log2 = scale * kLog2e;
-    p.total_wg = nq * p.n_hg * v.n_sp;
-    if (p.total_wg > 0x7fffffffLL) return SA_ERR_SHAPE;
+    const int64_t total = nq * p.n_hg * v.n_sp;
+    if (total > 0x7fffffffLL) return SA_ERR_SHAPE;
+    p.total_wg = (int32_t)total;
     hipStream_t hs = (hipStream_t)stream;
     hipError_t e;
-    switch (d) {
-        case 64: e = launch_d<64>(p, v.wh, v.wr, hs); break;
-        case 128: e = launch_d<128>(p, v.wh, v.wr, hs); break;
-        case 256: e = launch_d<256>(p, v.wh, v.wr, hs); break;
-        default: e = launch_d<512>(p, v.wh, v.wr, hs); break;
+    if (v.kernel == SA_KERNEL_DECODE) {
+        switch (d) {
+            case 64: e = launch_decode<64>(p, hs); break;
+            case 128: e = launch_decode<128>(p, hs); break;
+            case 256: e = launch_decode<256>(p, hs); break;
+            default: e = launch_decode<512>(p, hs); break;
+        }
+    } else {
+        switch (d) {
+            case 64: e = launch_wide<64>(p, hs); break;
+            case 128: e = launch_wide<128>(p, hs); break;
+            case 256: e = launch_wide<256>(p, hs); break;
+            default: e = launch_wide<512>(p, hs); break;
+        }
     }
     if (e != hipSuccess) return SA_ERR_HIP;
     if (v.n_sp > 1) {
@@ -579,15 +834,15 @@ sa_status run_sparse_attn(const uint16_t *q, const uint16_t *kv, const float *si
 extern "C" size_t sa_sparse_attn_workspace_bytes(int64_t b, int64_t s, int32_t h, int32_t d, int32_t topk) {
     if (b < 0 || s < 0 || h <= 0 || topk < 0 || !valid_d(d)) return 0;
     Variant v;
-    if (resolve_variant(b * s, h, topk, 0, 0, 0, &v) != SA_OK) return 0;
+    if (resolve_variant(b * s, h, topk, 0, 0, &v) != SA_OK) return 0;
     return workspace_for(v, b * s, h, d);
 }
 
 extern "C" size_t sa_sparse_attn_workspace_bytes_ex(int64_t b, int64_t s, int32_t h, int32_t d, int32_t topk,
-                                                    int32_t heads_per_wg, int32_t row_waves, int32_t splits) {
+                                                    int32_t kernel, int32_t splits) {
     if (b < 0 || s < 0 || h <= 0 || topk < 0 || !valid_d(d)) return 0;
     Variant v;
-    if (resolve_variant(b * s, h, topk, heads_per_wg, row_waves, splits, &v) != SA_OK) return 0;
+    if (resolve_variant(b * s, h, topk, kernel, splits, &v) != SA_OK) return 0;
     return workspace_for(v, b * s, h, d);
 }
 
@@ -596,14 +851,13 @@ extern "C" sa_status sa_sparse_attn(const uint16_t *q, const uint16_t *kv, const
                                     int64_t rows, int32_t topk, float scale, uint16_t *out, void *workspace,
                                     size_t workspace_bytes, void *stream) {
     return run_sparse_attn(q, kv, sink, idx, b, s, h, d, rows, topk, scale, out, workspace, workspace_bytes,
-                           stream, 0, 0, 0);
+                           stream, 0, 0);
 }
 
 extern "C" sa_status sa_sparse_attn_ex(const uint16_t *q, const uint16_t *kv, const float *sink,
                                        const int32_t *idx, int64_t b, int64_t s, int32_t h, int32_t d,
                                        int64_t rows, int32_t topk, float scale, uint16_t *out, void *workspace,
-                                       size_t workspace_bytes, void *stream, int32_t heads_per_wg,
-                                       int32_t row_waves, int32_t splits) {
+                                       size_t workspace_bytes, void *stream, int32_t kernel, int32_t splits) {
     return run_sparse_attn(q, kv, sink, idx, b, s, h, d, rows, topk, scale, out, workspace, workspace_bytes,
-                           stream, heads_per_wg, row_waves, splits);
+                           stream, kernel, splits);
 }

@@ -16,6 +16,7 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 #define SA_LDS __attribute__((address_space(3)))
 
@@ -23,16 +24,13 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// Round-to-nearest-even f32 -> bf16 bits (NaN stays NaN).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-// Two f32 -> packed pair of bf16 (low half = a), round to nearest even.
+// Two f32 -> packed pair of bf16 (low half = a), round to nearest even: one
+// gfx950 v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const SA_LDS void *p) {

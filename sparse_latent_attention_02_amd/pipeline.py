@@ -1,0 +1,99 @@
+"""One step of the sparse-attention hot path on the GPU, for the five workloads.
+
+A step is what one layer does per forward call on its attention inputs:
+  1. new KV rows are rounded through fp8 in place and written into the
+     sliding-window ring (sa_window_kv_update);
+  2. the window slot lists are built (sa_window_topk_idxs), straight into the
+     leading columns of the index buffer;
+  3. compressed positions, when the workload has them, are appended after the
+     window columns, shifted past the window rows (sa_append_compressed_idxs);
+  4. sparse attention over the selected rows (sa_sparse_attn).
+Everything runs through the C ABI on the current stream; torch only allocates.
+
+KV rows that exist before the step -- the ring contents at a decode step and
+the compressed cache -- are rounded through fp8 once in ``prepare``, as the cache
+holds them after earlier steps.
+"""
+from __future__ import annotations
+
+from types import SimpleNamespace
+
+import torch
+
+from . import sparse_attn, window_kv_update, window_topk_idxs, append_compressed_idxs, act_quant_fp8_
+from . import workspace_bytes
+from .workloads import WORKLOADS
+
+
+def prepare(wid: int, raw: dict, device: str = "cuda") -> SimpleNamespace:
+    w = WORKLOADS[wid]
+    st = SimpleNamespace(w=w, wid=wid)
+    st.sink = raw["sink"].to(device)
+    if wid == 1:
+        st.q_prefill = raw["q_prefill"].to(device)
+        st.q_dec = raw["q_dec"].to(device)
+        st.kv_prefill_raw = raw["kv_prefill"].to(device)
+        st.kv_dec_raw = raw["kv_dec"].to(device)
+        return st
+    st.q = raw["q"].to(device)
+    st.kv = raw["kv"].to(device)
+    st.out = torch.empty_like(st.q)
+    st.idx = torch.empty((w.b, w.s, w.topk), dtype=torch.int32, device=device)
+    st.comp = raw["comp"].to(device) if raw["comp"] is not None else None
+    if w.start_pos > 0:
+        act_quant_fp8_(st.kv)                              # ring + compressed cache before the step
+        slot = w.start_pos % w.window
+        st.new_rows = raw["kv"][:, slot:slot + 1].contiguous().to(device)  # this step's token, raw
+    else:
+        if w.rows > w.win_rows:
+            for bi in range(w.b):                          # compressed cache (produced upstream)
+                act_quant_fp8_(st.kv[bi, w.win_rows:])
+        st.chunk = st.kv[:, : w.win_rows] if w.b == 1 else None
+        assert st.chunk is not None and st.chunk.is_contiguous()
+        st.ring = torch.zeros((w.b, w.window, w.d), dtype=torch.bfloat16, device=device)
+    nws = workspace_bytes(w.b, w.s, w.h, w.d, w.topk)
+    st.ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=device)
+    return st
+
+
+def update_and_index(st: SimpleNamespace) -> None:
+    """Steps 1-3: ring update (with the fp8 round trip) and the index list."""
+    w = st.w
+    if w.start_pos > 0:
+        window_kv_update(st.kv, st.new_rows, w.start_pos, window=w.window)
+    else:
+        window_kv_update(st.ring, st.chunk, 0)
+    window_topk_idxs(w.window, w.b, w.s, w.start_pos, out=st.idx)
+    if st.comp is not None:
+        append_compressed_idxs(st.idx, w.win_cols, st.comp, w.win_rows)
+
+
+def attend(st: SimpleNamespace) -> torch.Tensor:
+    """Step 4."""
+    w = st.w
+    return sparse_attn(st.q, st.kv, st.sink, st.idx, w.scale, out=st.out, workspace=st.ws)
+
+
+def step(st: SimpleNamespace) -> torch.Tensor:
+    update_and_index(st)
+    return attend(st)
+
+
+def ring_run(st: SimpleNamespace) -> dict:
+    """Workload 1: prefill of 12 tokens, then decode positions 12 and 13, through one
+    8-slot ring.  Returns the outputs and the ring after each decode step."""
+    w = st.w
+    dev = st.sink.device
+    ring = torch.zeros((1, w.window, w.d), dtype=torch.bfloat16, device=dev)
+    chunk = st.kv_prefill_raw.clone()
+    window_kv_update(ring, chunk, 0)                      # chunk rounded in place, last 8 into the ring
+    res = {"ring_after_prefill": ring.clone()}
+    idx = window_topk_idxs(w.window, 1, w.s, 0, device=dev)
+    res["prefill"] = sparse_attn(st.q_prefill, chunk, st.sink, idx, w.scale)
+    for i, pos in enumerate((12, 13)):
+        row = st.kv_dec_raw[i].clone()                     # [1][1][d]
+        window_kv_update(ring, row, pos)
+        idx = window_topk_idxs(w.window, 1, 1, pos, device=dev)
+        res[f"decode{pos}"] = sparse_attn(st.q_dec[i], ring, st.sink, idx, w.scale)
+        res[f"ring{pos}"] = ring.clone()
+    return res

@@ -110,12 +110,11 @@ SMALL = [
     (12, 1, 1, 16, 128, 80, 70, 0.1),
     (13, 1, 1, 16, 256, 80, 70, 0.1),
 ]
-VARIANTS = [None, (16, 1, 1), (32, 1, 1), (64, 1, 1), (16, 2, 1), (32, 2, 1), (16, 4, 1), (64, 1, 3),
-            (16, 1, 2), (32, 1, 5)]
+VARIANTS = [None, (1, 1), (1, 2), (1, 3), (1, 7), (2, 1), (2, 2), (2, 5)]
 
 
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: f"s{c[0]}_h{c[3]}_d{c[4]}_k{c[6]}")
-@pytest.mark.parametrize("variant", VARIANTS, ids=lambda v: "auto" if v is None else "v%d_%d_%d" % v)
+@pytest.mark.parametrize("variant", VARIANTS, ids=lambda v: "auto" if v is None else "k%d_sp%d" % v)
 def test_sparse_attn_small(case, variant):
     seed, b, s, h, d, rows, topk, p_inv = case
     c = wl.small_case(seed, b, s, h, d, rows, topk, p_inv)
@@ -137,7 +136,7 @@ def test_sparse_attn_edge_cases():
     assert_parity(got, ref, "sink -inf")
     assert not np.any(got[0])               # all -1 with no sink term: 0, not NaN
     c0 = dict(c, idx=torch.zeros((2, 3, 0), dtype=torch.int32))
-    for v in (None, (16, 4, 1), (64, 1, 2)):
+    for v in (None, (1, 1), (1, 2), (2, 1), (2, 3)):
         got = bits(sa.sparse_attn(to_dev(c0["q"]), to_dev(c0["kv"]), to_dev(c0["sink"]), to_dev(c0["idx"]),
                                   0.1, variant=v))
         assert not np.any(got)
@@ -178,10 +177,12 @@ def test_sparse_attn_argument_errors():
     assert L.sa_window_topk_idxs(8, 1, 4, 3, None, 8, None) == sa.SA_ERR_UNSUPPORTED
     out = torch.zeros((1, 12, 8), dtype=torch.int32, device=DEV)
     assert L.sa_window_topk_idxs(8, 1, 12, 0, out.data_ptr(), 7, None) == sa.SA_ERR_SHAPE
-    # forced split without workspace
+    # forced split (64 entries -> two 32-entry pieces) without workspace; unknown kernel
     q = torch.zeros((1, 1, 16, 512), dtype=torch.bfloat16, device=DEV)
     kv = torch.zeros((1, 4, 512), dtype=torch.bfloat16, device=DEV)
-    assert L.sa_sparse_attn_ex(q.data_ptr(), kv.data_ptr(), sink.data_ptr(), idx.data_ptr(), 1, 1, 16, 512, 4, 4,
-                               0.1, q.data_ptr(), None, 0, None, 16, 1, 2) == sa.SA_ERR_SHAPE
-    assert L.sa_sparse_attn_ex(q.data_ptr(), kv.data_ptr(), sink.data_ptr(), idx.data_ptr(), 1, 1, 16, 512, 4, 4,
-                               0.1, q.data_ptr(), None, 0, None, 16, 4, 2) == sa.SA_ERR_UNSUPPORTED
+    idx = torch.zeros((1, 1, 64), dtype=torch.int32, device=DEV)
+    assert sa.workspace_bytes(1, 1, 16, 512, 64, (1, 2)) > 0
+    assert L.sa_sparse_attn_ex(q.data_ptr(), kv.data_ptr(), sink.data_ptr(), idx.data_ptr(), 1, 1, 16, 512, 4, 64,
+                               0.1, q.data_ptr(), None, 0, None, 1, 2) == sa.SA_ERR_SHAPE
+    assert L.sa_sparse_attn_ex(q.data_ptr(), kv.data_ptr(), sink.data_ptr(), idx.data_ptr(), 1, 1, 16, 512, 4, 64,
+                               0.1, q.data_ptr(), None, 0, None, 9, 1) == sa.SA_ERR_UNSUPPORTED
