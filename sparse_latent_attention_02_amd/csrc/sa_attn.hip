@@ -432,12 +432,15 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
 // ------------------------------------------------------------------ decode --
 //
 // Decode kernel: one workgroup of four wavefronts per (query, group of 16
-// heads), for short index lists.  A stage holds up to 128 gathered rows; the
-// four wavefronts split the rows for the scores (S^T[32 rows][16 heads] each,
-// MFMA 16x16x32), exchange the per-head maxima and the bf16 weights P through
-// LDS, then split the head dim for O^T[128 d][16 heads] = V^T P^T over all the
-// stage's rows.  Every gathered row is read from LDS once as K and once as V,
-// and no partial result leaves the workgroup.
+// heads), for short index lists.  A stage covers 128 index entries; each
+// wavefront loads its 32 entries into registers and copies their rows straight
+// into LDS (a zero row for a -1 entry, which then contributes nothing), so no
+// list compaction sits on the latency path.  The wavefronts split the rows for
+// the scores (S^T[32 rows][16 heads] each, MFMA 16x16x32), exchange the
+// per-head maxima and the bf16 weights P through LDS, then split the head dim
+// for O^T[128 d][16 heads] = V^T P^T over all the stage's rows.  Every gathered
+// row is read from LDS once as K and once as V, and no partial result leaves
+// the workgroup.
 template <int D>
 struct DecodeCfg {
     static constexpr int NW = 4;
@@ -462,8 +465,6 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) char pbuf[16 * C::PRS];
     __shared__ float smax[C::NW][16];
     __shared__ float ssum[C::NW][16];
-    __shared__ int list[kListCap];
-    __shared__ int wcnt[kListCap / 64];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -481,8 +482,10 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
     const int lo = (int)sp * p.split_len;
     const int hi = min(p.topk, lo + p.split_len);
     const int32_t *idxq = p.idx + (int64_t)qi * p.topk;
-    Compactor<C::THREADS> cmp;
-    cmp.load(idxq, lo, min(hi, lo + kListCap));
+    // this wave's 32 index entries of a stage sit in lanes 0..31 (mirrored in 32..63);
+    // the first stage's go in flight before anything else: they head the critical path
+    const int eoff = 32 * wave + (lane & 31);
+    int vnext = lo + eoff < hi ? idxq[lo + eoff] : -1;
 
     const int head = (int)hg * 16 + n;
     const bool head_ok = head < p.h;
@@ -510,95 +513,93 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
     // weighted-sum operand (transposing read): rows 32 ks + 8 g + 4 rd + p/4, d 16 dt + 4 (p%4) of this wave's quarter
     const SA_LDS char *vb = lds + (8 * g + (n >> 2)) * C::RS + 2 * C::DQ * wave + 8 * (n & 3);
 
-    for (int c0 = lo; c0 < hi; c0 += kListCap) {
-        const int c1 = min(hi, c0 + kListCap);
-        if (c0 != lo) cmp.load(idxq, c0, c1);
-        const int nv = cmp.pack(p.rows, list, wcnt);
-        if (nv == 0) continue;
-        const int last_row = list[nv - 1];
-        for (int ebase = 0; ebase < nv; ebase += C::ROWS) {
-            // ---- gather this stage: each wave copies 32 rows, one row per instruction ----
-            {
-                const int e0 = ebase + wave * C::RPW;
-                int rowv[C::RPW];
-#pragma unroll
-                for (int u = 0; u < C::RPW; u += 4) {
-                    const i32x4_t r4 = *reinterpret_cast<const SA_LDS i32x4_t *>((const SA_LDS int *)list + e0 + u);
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) rowv[u + c] = e0 + u + c < nv ? r4[c] : last_row;
-                }
-#pragma unroll
-                for (int u = 0; u < C::RPW; ++u)
-                    if (C::CH == 64 || lane < C::CH)
-                        dma_16B(kvb + (int64_t)rowv[u] * D + lane * 8,
-                                __builtin_amdgcn_readfirstlane(smem_base + (wave * C::RPW + u) * C::RS));
-                wait_vmcnt_barrier<0>();
-            }
-
-            // ---- scores S^T for this wave's 32 rows: two 16-row tiles ----
-            f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks) {
-                const bf16x8_t a0 = lds_read_b128(kb + 64 * ks);
-                const bf16x8_t a1 = lds_read_b128(kb + 16 * C::RS + 64 * ks);
-                s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qreg[ks], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qreg[ks], s1, 0, 0, 0);
-            }
-            // value i of tile t in lane (g, n): row 32 wave + 16 t + 4 g + i, head n
-            float sv[8];
-            float mx = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = ebase + 32 * wave + 4 * g + i;
-                sv[i] = r < nv ? s0[i] * p.scale_log2 : -INFINITY;
-                sv[4 + i] = r + 16 < nv ? s1[i] * p.scale_log2 : -INFINITY;
-                mx = fmaxf(mx, fmaxf(sv[i], sv[4 + i]));
-            }
-            mx = fmaxf(mx, shfl_xor_f32(mx, 16));
-            mx = fmaxf(mx, shfl_xor_f32(mx, 32));
-            if (g == 0) smax[wave][n] = mx;
-            lds_barrier();
-            float ms = fmaxf(fmaxf(smax[0][n], smax[1][n]), fmaxf(smax[2][n], smax[3][n]));
-            if (__ballot(ms > m_ref + kRescaleSlack)) {  // same decision in every wave
-                const float m_new = fmaxf(m_ref, ms);
-                if (__ballot(m_ref > -1e29f)) {
-                    const float alpha = exp2_fast(m_ref - m_new);
-#pragma unroll
-                    for (int dt = 0; dt < C::DT; ++dt) acc_o[dt] *= alpha;
-                    l_run *= alpha;
-                }
-                m_ref = m_new;
-            }
-            // weights -> bf16 -> P[head][row] in LDS (rows 32 wave + 16 t + 4 g + 0..3)
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const uint32_t b0 = pack_bf16x2(exp2_fast(sv[4 * t] - m_ref), exp2_fast(sv[4 * t + 1] - m_ref));
-                const uint32_t b1 = pack_bf16x2(exp2_fast(sv[4 * t + 2] - m_ref), exp2_fast(sv[4 * t + 3] - m_ref));
-                l_run += __uint_as_float(b0 << 16) + __uint_as_float(b0 & 0xffff0000u) +
-                         __uint_as_float(b1 << 16) + __uint_as_float(b1 & 0xffff0000u);
-                *reinterpret_cast<SA_LDS u32x2_t *>((SA_LDS char *)pl + n * C::PRS + 2 * (32 * wave + 16 * t + 4 * g)) =
-                    u32x2_t{b0, b1};
-            }
-            lds_barrier();
-
-            // ---- O^T[this wave's d quarter][16 heads] += V^T P^T over the stage's rows ----
-            const int nks = min(C::ROWS, nv - ebase + 31) / 32;  // 32-row k-steps holding data
-#pragma unroll
-            for (int ks = 0; ks < C::ROWS / 32; ++ks) {
-                if (ks < nks) {
-                    const bf16x8_t pb = lds_read_b128(pl + n * C::PRS + 2 * (32 * ks + 8 * g));
-#pragma unroll
-                    for (int dt = 0; dt < C::DT; ++dt) {
-                        const i16x4_t lo4 = lds_read_tr16(vb + (32 * ks) * C::RS + 32 * dt);
-                        const i16x4_t hi4 = lds_read_tr16(vb + (32 * ks + 4) * C::RS + 32 * dt);
-                        const bf16x8_t a =
-                            __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-                        acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, acc_o[dt], 0, 0, 0);
-                    }
-                }
-            }
-            lds_barrier();  // buffer and weights free for the next stage
+    for (int ebase = lo; ebase < hi; ebase += C::ROWS) {
+        // ---- gather: valid entries (0 <= v < rows) are copied row by row straight
+        //      from the index registers; other slots get a zero row, which adds nothing ----
+        const int v = vnext;
+        const bool ok = v >= 0 && (int64_t)v < p.rows;
+        const uint64_t okm = __ballot(ok) & 0xffffffffull;   // bit r: row 32 wave + r valid
+        if (ebase + C::ROWS < hi) {                           // next stage's entries in flight
+            const int e = ebase + C::ROWS + eoff;
+            vnext = e < hi ? idxq[e] : -1;
         }
+#pragma unroll
+        for (int u = 0; u < C::RPW; ++u) {
+            const uint32_t dst = smem_base + (wave * C::RPW + u) * C::RS;
+            if ((okm >> u) & 1) {
+                const int row = __builtin_amdgcn_readlane(v, u);
+                if (C::CH == 64 || lane < C::CH)
+                    dma_16B(kvb + (int64_t)row * D + lane * 8, __builtin_amdgcn_readfirstlane(dst));
+            } else if (C::CH == 64 || lane < C::CH) {
+                *reinterpret_cast<SA_LDS u32x4_t *>((SA_LDS char *)smem + (wave * C::RPW + u) * C::RS + 16 * lane) =
+                    u32x4_t{0u, 0u, 0u, 0u};
+            }
+        }
+        wait_all_barrier();  // copied and zeroed rows of every wave in place
+
+        // ---- scores S^T for this wave's 32 rows: two 16-row tiles ----
+        f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            const bf16x8_t a0 = lds_read_b128(kb + 64 * ks);
+            const bf16x8_t a1 = lds_read_b128(kb + 16 * C::RS + 64 * ks);
+            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qreg[ks], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qreg[ks], s1, 0, 0, 0);
+        }
+        // value i of tile t in lane (g, n): row 32 wave + 16 t + 4 g + i, head n
+        float sv[8];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g + i;
+            sv[i] = (okm >> r) & 1 ? s0[i] * p.scale_log2 : -INFINITY;
+            sv[4 + i] = (okm >> (r + 16)) & 1 ? s1[i] * p.scale_log2 : -INFINITY;
+            mx = fmaxf(mx, fmaxf(sv[i], sv[4 + i]));
+        }
+        mx = fmaxf(mx, shfl_xor_f32(mx, 16));
+        mx = fmaxf(mx, shfl_xor_f32(mx, 32));
+        if (g == 0) smax[wave][n] = mx;
+        lds_barrier();
+        const float ms = fmaxf(fmaxf(smax[0][n], smax[1][n]), fmaxf(smax[2][n], smax[3][n]));
+        if (__ballot(ms > m_ref + kRescaleSlack)) {  // same decision in every wave
+            const float m_new = fmaxf(m_ref, ms);
+            if (__ballot(m_ref > -1e29f)) {
+                const float alpha = exp2_fast(m_ref - m_new);
+#pragma unroll
+                for (int dt = 0; dt < C::DT; ++dt) acc_o[dt] *= alpha;
+                l_run *= alpha;
+            }
+            m_ref = m_new;
+        }
+        // weights -> bf16 -> P[head][row] in LDS (rows 32 wave + 16 t + 4 g + 0..3)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint32_t b0 = pack_bf16x2(exp2_fast(sv[4 * t] - m_ref), exp2_fast(sv[4 * t + 1] - m_ref));
+            const uint32_t b1 = pack_bf16x2(exp2_fast(sv[4 * t + 2] - m_ref), exp2_fast(sv[4 * t + 3] - m_ref));
+            l_run += __uint_as_float(b0 << 16) + __uint_as_float(b0 & 0xffff0000u) + __uint_as_float(b1 << 16) +
+                     __uint_as_float(b1 & 0xffff0000u);
+            *reinterpret_cast<SA_LDS u32x2_t *>((SA_LDS char *)pl + n * C::PRS + 2 * (32 * wave + 16 * t + 4 * g)) =
+                u32x2_t{b0, b1};
+        }
+        lds_barrier();
+
+        // ---- O^T[this wave's d quarter][16 heads] += V^T P^T over the stage's rows ----
+        const int nks = min(C::ROWS, hi - ebase + 31) / 32;  // 32-row k-steps holding entries
+#pragma unroll
+        for (int ks = 0; ks < C::ROWS / 32; ++ks) {
+            if (ks < nks) {
+                const bf16x8_t pb = lds_read_b128(pl + n * C::PRS + 2 * (32 * ks + 8 * g));
+#pragma unroll
+                for (int dt = 0; dt < C::DT; ++dt) {
+                    const i16x4_t lo4 = lds_read_tr16(vb + (32 * ks) * C::RS + 32 * dt);
+                    const i16x4_t hi4 = lds_read_tr16(vb + (32 * ks + 4) * C::RS + 32 * dt);
+                    const bf16x8_t a =
+                        __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+                    acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, acc_o[dt], 0, 0, 0);
+                }
+            }
+        }
+        lds_barrier();  // buffer and weights free for the next stage
     }
 
     // this wave's share of the sum: add the four lane groups, then the four waves

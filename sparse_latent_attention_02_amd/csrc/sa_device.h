@@ -57,6 +57,12 @@ __device__ __forceinline__ void wait_vmcnt_barrier() {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
+// Wait for all of this wave's memory operations (copies into LDS and LDS
+// writes), then barrier the workgroup.
+__device__ __forceinline__ void wait_all_barrier() {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" : : : "memory");
+}
+
 // Wait for this wave's LDS operations, then barrier the workgroup.
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
