@@ -4,7 +4,9 @@
 A step is one pass of the whole path over one batch of synthetic input: the new
 KV rows rounded through fp8 and written into the window ring, the window slot
 lists built, compressed positions appended (when the workload has them) and
-the sparse attention itself -- all through the C ABI on one stream.
+the sparse attention itself -- all through the C ABI on one stream.  Decode
+workloads run the step as one launch (sa_sparse_attn_decode_step, the lists
+built inside the attention kernel); ``--unfused`` times the separate calls.
 
 Default workload: decode over the window ring, batch 64 single-query steps at
 position 5000, 64 heads, head dim 512, 128-slot ring (the configuration the
@@ -52,15 +54,21 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration under rocprofv3)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="decode: run the step as separate calls (ring update, lists, attention) "
+                         "instead of the one-launch decode step")
     ap.add_argument("--no-graphs", dest="graphs", action="store_false",
                     help="launch every step eagerly from Python instead of replaying HIP graphs")
     return ap.parse_args()
 
 
-def algorithmic_work(w, idx_sets):
+def algorithmic_work(w, idx_sets, fused=False):
     """Algorithmic bytes and flops of one attention launch (valid entries only).
     Decode: every valid gathered row is HBM traffic (rows differ per sequence).
-    Prefill: the unique KV rows referenced are read once; repeats come from cache."""
+    Prefill: the unique KV rows referenced are read once; repeats come from cache.
+    Fused decode step: the list is written instead of read (compressed entries
+    still read), and the new row is read once and written once into the ring
+    (it enters the attention from registers instead of the ring)."""
     import torch
     idx = idx_sets[0]
     valid = int((idx >= 0).sum().item())
@@ -77,22 +85,25 @@ def algorithmic_work(w, idx_sets):
             u = idx[bi].flatten()
             uniq += int(torch.unique(u[u >= 0]).numel())
         kv_bytes = uniq * w.d * 2
+    if fused:
+        idx_bytes += w.b * w.s * w.n_comp * 4
+        kv_bytes += w.b * w.d * 2
     total = q_bytes + o_bytes + idx_bytes + sink_bytes + kv_bytes
     return dict(bytes=total, flops=flops, valid=valid, kv_bytes=kv_bytes)
 
 
 def source_sha():
     h = hashlib.sha256()
-    for f in ("sa_attn.hip", "sa_device.h"):
+    for f in ("sa_attn.hip", "sa_device.h", "sa_fp8.h"):
         with open(os.path.join(HERE, "sparse_latent_attention_02_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(wid):
+def measured_traffic(wid, fused):
     """HBM bytes per attention launch from the committed rocprofv3 counter summary,
     if it was taken on the current kernel source; else None."""
-    path = os.path.join(HERE, "profiles", f"attn_w{wid}_hbm_traffic.json")
+    path = os.path.join(HERE, "profiles", f"attn_w{wid}{'' if fused else '_unfused'}_hbm_traffic.json")
     try:
         with open(path) as fh:
             t = json.load(fh)
@@ -216,7 +227,10 @@ def main():
     sets = [pipeline.prepare(args.workload, raw0)]
     pipeline.update_and_index(sets[0])
     torch.cuda.synchronize()
-    work = algorithmic_work(w, [sets[0].idx])
+    fused = w.start_pos > 0 and not args.unfused
+    step_fn = pipeline.step_fused if fused else pipeline.step
+    kern_fn = pipeline.step_fused if fused else pipeline.attend    # the dominant kernel's launch
+    work = algorithmic_work(w, [sets[0].idx], fused)
     n_sets = args.sets or max(1, min(48, math.ceil(2 * MALL_BYTES / work["bytes"])))
     for k in range(1, n_sets):
         sets.append(pipeline.prepare(args.workload, wl.generate(args.workload, seed_offset=97 * k)))
@@ -237,7 +251,7 @@ def main():
     # ---- warmup (eager), then one HIP graph per input set for the step and for
     #      the attention launch alone: replays keep the host out of the timing ----
     for i in range(args.warmup):
-        pipeline.step(sets[i % n_sets])
+        step_fn(sets[i % n_sets])
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     if args.graphs:
@@ -250,9 +264,9 @@ def main():
                 for i in ids:
                     fn(sets[i])
             return g
-        full = capture(pipeline.step, range(n_sets))
+        full = capture(step_fn, range(n_sets))
         rem = args.steps % n_sets
-        tail = capture(pipeline.step, range(rem)) if rem else None
+        tail = capture(step_fn, range(rem)) if rem else None
 
         def run_steps(k):
             for _ in range(k // n_sets):
@@ -260,7 +274,7 @@ def main():
             if k % n_sets:
                 assert k % n_sets == rem
                 tail.replay()
-        attn_graph = capture(pipeline.attend, range(n_sets))
+        attn_graph = capture(kern_fn, range(n_sets))
         n_attn_reps = max(1, math.ceil(args.steps / n_sets))
         run_attn = lambda: [attn_graph.replay() for _ in range(n_attn_reps)]
         n_attn = n_attn_reps * n_sets
@@ -268,9 +282,9 @@ def main():
     else:
         def run_steps(k):
             for i in range(k):
-                pipeline.step(sets[i % n_sets])
+                step_fn(sets[i % n_sets])
         n_attn = max(args.steps, n_sets)
-        run_attn = lambda: [pipeline.attend(sets[i % n_sets]) for i in range(n_attn)]
+        run_attn = lambda: [kern_fn(sets[i % n_sets]) for i in range(n_attn)]
         launch_desc = "eager"
     run_steps(args.steps)
     torch.cuda.synchronize()
@@ -309,7 +323,7 @@ def main():
         achieved = work["flops"] / (attn_mean / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
-    roof["traffic"] = measured_traffic(args.workload)
+    roof["traffic"] = measured_traffic(args.workload, fused or w.start_pos == 0)
     roof["algorithmic_bytes"] = work["bytes"]
     roof["algorithmic_flops"] = work["flops"]
     roof["kernel_ms_mean"] = round(attn_mean, 5)
@@ -331,6 +345,7 @@ def main():
         "config": {"workload": w.name, "batch": w.b, "queries_per_seq": w.s, "heads": w.h, "head_dim": w.d,
                    "topk": w.topk, "kv_rows_per_seq": w.rows, "valid_entries": work["valid"],
                    "input_sets": n_sets, "launch": launch_desc,
+                   "step": "one-launch decode step" if fused else "separate calls",
                    "parallelism": "single GPU"},
         "roofline": roof,
         "wall_s": round(wall, 3),

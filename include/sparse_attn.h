@@ -196,6 +196,53 @@ sa_status sa_sparse_attn_ex(const uint16_t *q, const uint16_t *kv, const float *
                             void *workspace, size_t workspace_bytes, void *stream,
                             int32_t kernel, int32_t splits);
 
+/* ------------------------------------------------------------------------
+ * One decode step in one launch -- [QLAT] Attention.forward at a decode step
+ * (the new KV row rounded through fp8 and written into the ring, the window
+ * list, the compressed indices concatenated after it, sparse_attn), [ATTEND]
+ * get_window_topk_idxs (decode branch), [ATTN-RS] ring-cache worked example.
+ *
+ * Same result as this sequence of calls, with seqlen = 1 and s = 1:
+ *   sa_window_kv_update(kv, rows, kv_new', b, window, d, start_pos, 1)
+ *   sa_window_topk_idxs(window, b, 1, start_pos, idx, window + kc)
+ *   sa_append_compressed_idxs(idx, window + kc, window, cidx, b, kc, window)
+ *   sa_sparse_attn(q, kv, sink, idx, b, 1, h, d, rows, window + kc, scale, out)
+ * except that kv_new is read only (kv_new' is a copy that gets rounded): the
+ * rounded row goes to ring slot start_pos % window of kv.  The list is built
+ * inside the attention kernel, the new row is rounded there and enters the
+ * attention from registers, so nothing of the list or the new row makes an
+ * extra trip through memory.
+ *
+ *   q       [b][h][d]      bf16  one query per sequence, at position start_pos
+ *   kv      [b][rows][d]   bf16  per sequence: rows [0, window) the ring, rows
+ *                                [window, rows) the compressed cache; slot
+ *                                start_pos % window is overwritten
+ *   kv_new  [b][d]         bf16  this step's latent row before the fp8 round trip
+ *   sink    [h]            f32
+ *   cidx    [b][kc]        int32 compressed positions (-1 = none); may be NULL
+ *                                when kc == 0; entry c addresses kv row window + c
+ *   idx_out [b][window+kc] int32 NULL, or receives the concatenated list (what
+ *                                the calls above would leave in idx)
+ *   out     [b][h][d]      bf16
+ * start_pos >= 1 (position 0 is a prefill: SA_ERR_UNSUPPORTED); window >= 1;
+ * rows >= window; d in {64, 128, 256, 512}; kc >= 0.  Pointers of bf16 data
+ * 16-byte aligned (else SA_ERR_SHAPE).  Tolerance, determinism and the index
+ * rules are those of sa_sparse_attn.  Of kv, only row start_pos % window of
+ * each sequence is written.
+ *
+ * kernel, splits: as for sa_sparse_attn_ex (0, 0 = automatic).  workspace: at
+ * least sa_sparse_attn_decode_step_workspace_bytes(b, h, d, window, kc, kernel,
+ * splits) bytes, 16-byte aligned (may be NULL when that is 0). */
+size_t sa_sparse_attn_decode_step_workspace_bytes(int64_t b, int32_t h, int32_t d, int32_t window, int32_t kc,
+                                                  int32_t kernel, int32_t splits);
+
+sa_status sa_sparse_attn_decode_step(const uint16_t *q, uint16_t *kv, const uint16_t *kv_new,
+                                     const float *sink, const int32_t *cidx, int32_t *idx_out,
+                                     int64_t b, int32_t h, int32_t d, int64_t rows, int32_t window,
+                                     int32_t kc, int64_t start_pos, float scale, uint16_t *out,
+                                     void *workspace, size_t workspace_bytes, void *stream,
+                                     int32_t kernel, int32_t splits);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,6 +11,7 @@ Names follow the C ABI:
   act_quant_fp8_                           -- fp8 (e4m3) round trip of bf16 rows, in place
   window_kv_update                         -- fp8 round trip of new rows + ring-cache write
   sparse_attn                              -- the attention itself
+  sparse_attn_decode_step                  -- a whole decode step (ring write, lists, attention) in one launch
 """
 from __future__ import annotations
 
@@ -57,8 +58,13 @@ def lib() -> ctypes.CDLL:
         L.sa_sparse_attn.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i64, i32, f32, vp, vp, sz, vp]
         L.sa_sparse_attn_ex.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i64, i32, f32, vp, vp, sz, vp,
                                         i32, i32]
+        L.sa_sparse_attn_decode_step_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, i32, i32]
+        L.sa_sparse_attn_decode_step_workspace_bytes.restype = sz
+        L.sa_sparse_attn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i64, i32, i32, i64, f32,
+                                                 vp, vp, sz, vp, i32, i32]
         for fn in ("sa_window_topk_idxs_shape", "sa_window_topk_idxs", "sa_append_compressed_idxs",
-                   "sa_act_quant_fp8_inplace", "sa_window_kv_update", "sa_sparse_attn", "sa_sparse_attn_ex"):
+                   "sa_act_quant_fp8_inplace", "sa_window_kv_update", "sa_sparse_attn", "sa_sparse_attn_ex",
+                   "sa_sparse_attn_decode_step"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -185,3 +191,59 @@ def sparse_attn(q: torch.Tensor, kv: torch.Tensor, sink: torch.Tensor, idx: torc
     else:
         _check("sa_sparse_attn_ex", lib().sa_sparse_attn_ex(*args, *variant))
     return out
+
+
+def decode_step_workspace_bytes(b: int, h: int, d: int, window: int, kc: int, variant: tuple | None = None) -> int:
+    k, sp = variant if variant is not None else (0, 0)
+    return int(lib().sa_sparse_attn_decode_step_workspace_bytes(b, h, d, window, kc, k, sp))
+
+
+def sparse_attn_decode_step(q: torch.Tensor, kv: torch.Tensor, kv_new: torch.Tensor, sink: torch.Tensor,
+                            window: int, start_pos: int, scale: float, cidx: torch.Tensor | None = None,
+                            out: torch.Tensor | None = None, idx_out: torch.Tensor | None = None,
+                            workspace: torch.Tensor | None = None, variant: tuple | None = None,
+                            stream=None) -> torch.Tensor:
+    """One decode step in one launch: kv_new [b][d] rounded through fp8 into ring slot
+    start_pos % window of kv [b][rows][d] (rows [0, window) = ring, compressed rows
+    after), the window list + cidx [b][kc] (+window) as the index list, sparse
+    attention of q [b][h][d] (or [b][1][h][d]).  kv_new is not modified.  ``idx_out``
+    ([b][window + kc] int32) receives the list when given."""
+    _dev(q, "q", torch.bfloat16)
+    _dev(kv, "kv", torch.bfloat16)
+    _dev(kv_new, "kv_new", torch.bfloat16)
+    _dev(sink, "sink", torch.float32)
+    b, rows, d = kv.shape
+    h = q.shape[-2]
+    if q.numel() != b * h * d or q.shape[0] != b or q.shape[-1] != d:
+        raise ValueError(f"q must be [{b}][{h}][{d}] (or [{b}][1][{h}][{d}]), got {tuple(q.shape)}")
+    if kv_new.numel() != b * d or kv_new.shape[0] != b:
+        raise ValueError(f"kv_new must be [{b}][{d}], got {tuple(kv_new.shape)}")
+    if sink.shape != (h,):
+        raise ValueError(f"sink must be [{h}]")
+    kc = 0
+    if cidx is not None:
+        _dev(cidx, "cidx", torch.int32)
+        kc = cidx.shape[-1]
+        if cidx.numel() != b * kc:
+            raise ValueError(f"cidx must be [{b}][kc], got {tuple(cidx.shape)}")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", torch.bfloat16)
+    if idx_out is not None:
+        _dev(idx_out, "idx_out", torch.int32)
+        if idx_out.numel() != b * (window + kc):
+            raise ValueError(f"idx_out must hold [{b}][{window + kc}]")
+    k, sp = variant if variant is not None else (0, 0)
+    need = decode_step_workspace_bytes(b, h, d, window, kc, variant)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("sa_sparse_attn_decode_step",
+           lib().sa_sparse_attn_decode_step(q.data_ptr(), kv.data_ptr(), kv_new.data_ptr(), sink.data_ptr(),
+                                            cidx.data_ptr() if cidx is not None else None,
+                                            idx_out.data_ptr() if idx_out is not None else None,
+                                            b, h, d, rows, window, kc, start_pos, float(scale), out.data_ptr(),
+                                            ws_ptr, ws_bytes, _stream(stream), k, sp))
+    return out
+

@@ -39,7 +39,7 @@
 //  6. sink fold, normalisation, bf16 staged through LDS and stored one row per
 //     wave instruction -- or, for split variants, f32 partials (running max,
 //     sum, unnormalised O) combined by a second pass.
-#include "sa_device.h"
+#include "sa_fp8.h"
 #include "../../include/sparse_attn.h"
 
 #include <algorithm>
@@ -71,7 +71,33 @@ struct AttnParams {
     int32_t n_sp;       // index splits
     int32_t split_len;  // index entries per split
     float scale_log2;   // softmax scale * log2(e)
+    // fused decode step only: the list is built in the kernel and the step's
+    // new latent row is rounded through fp8 and written into its ring slot
+    const uint16_t *kv_new;  // [nq][d] this step's raw latent rows
+    uint16_t *kv_ring;       // == kv, writable: ring slot new_slot receives the rounded row
+    const int32_t *cidx;     // [nq][kc] compressed positions (-1 = none)
+    int32_t *idx_out;        // [nq][topk] concatenated list written out, or null
+    int64_t pos;             // position of the step's token (start_pos >= 1)
+    int32_t window;          // ring slots = window-list columns
+    int32_t kc;              // compressed columns
+    int32_t wbase;           // (pos + 1) % window: slot of the oldest entry
+    int32_t new_slot;        // pos % window: slot of the new row (list entry window - 1)
 };
+
+// Entry e of a decode step's concatenated list: the ring listed oldest first,
+// -1 for slots not yet written ("DeepSeek V4.1 ... attention / attend",
+// get_window_topk_idxs, decode branch), then the compressed positions shifted
+// past the ring rows, -1 kept ("... / query-latent", Attention.forward and the
+// Indexer tail).
+__device__ __forceinline__ int step_entry(const AttnParams &p, uint32_t qi, int e) {
+    if (e < p.window) {
+        int slot = p.wbase + e;
+        if (slot >= p.window) slot -= p.window;
+        return (int64_t)slot <= p.pos ? slot : -1;
+    }
+    const int c = p.cidx[(int64_t)qi * p.kc + (e - p.window)];
+    return c < 0 ? -1 : (int)((uint32_t)c + (uint32_t)p.window);
+}
 
 __device__ __forceinline__ bf16x8_t lds_read_b128(const SA_LDS char *p) {
     return *reinterpret_cast<const SA_LDS bf16x8_t *>(p);
@@ -104,11 +130,22 @@ struct Compactor {
     static constexpr int NW = NT / 64;
     int v[K];
 
-    __device__ __forceinline__ void load(const int32_t *__restrict__ idxq, int c0, int c1) {
+    // fetch(e) gives list entry e (a load, or an entry built in place)
+    template <class F>
+    __device__ __forceinline__ void load(F fetch, int c0, int c1) {
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int e = c0 + k * NT + (int)threadIdx.x;
-            v[k] = e < c1 ? idxq[e] : -1;
+            v[k] = e < c1 ? fetch(e) : -1;
+        }
+    }
+
+    // the raw entries of [c0, c1) written out (fused decode step, one head group)
+    __device__ __forceinline__ void store(int32_t *out, int c0, int c1) const {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int e = c0 + k * NT + (int)threadIdx.x;
+            if (e < c1) out[e] = v[k];
         }
     }
 
@@ -174,7 +211,7 @@ struct WideCfg {
     static_assert(RPW % 4 == 0 && KS >= 4 && DT >= 1, "tiling");
 };
 
-template <int D>
+template <int D, bool FUSED>
 __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const AttnParams p) {
     using C = WideCfg<D>;
     __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
@@ -183,7 +220,7 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
     __shared__ int wcnt[kListCap / 64];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave values in SGPRs
     const int lane = tid & 63;
     const int hf = lane >> 5;     // which half of a 32-wide MFMA k (or m) block this lane feeds
     const int n = lane & 31;      // head (B / C column) or row (A row) of this lane
@@ -199,10 +236,16 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
 
     const int lo = (int)sp * p.split_len;
     const int hi = min(p.topk, lo + p.split_len);
-    const int32_t *idxq = p.idx + (int64_t)qi * p.topk;
+    const int32_t *idxq = FUSED ? nullptr : p.idx + (int64_t)qi * p.topk;
+    auto fetch = [&](int e) -> int { return FUSED ? step_entry(p, qi, e) : idxq[e]; };
+    // fused step: the new row's entry (window - 1) in this workgroup's range
+    const bool has_new = FUSED && p.window - 1 >= lo && p.window - 1 < hi;
+    u32x4_t new_raw = {0u, 0u, 0u, 0u};
+    if (has_new && wave == 0 && (C::CH == 64 || lane < C::CH))
+        new_raw = *reinterpret_cast<const u32x4_t *>(p.kv_new + (int64_t)qi * D + lane * 8);
     // the first index chunk goes in flight before anything else: it heads the critical path
     Compactor<C::THREADS> cmp;
-    cmp.load(idxq, lo, min(hi, lo + kListCap));
+    cmp.load(fetch, lo, min(hi, lo + kListCap));
 
     const int head = ((int)hg * 2 + hw) * 32 + n;
     const bool head_ok = head < p.h;
@@ -232,9 +275,21 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
     const int voff = (4 * hf + (p16 >> 2)) * C::RS + slice + 16 * (2 * ((lane >> 4) & 1) + ((p16 & 3) >> 1)) +
                      ((p16 & 1) << 3);
 
+    if (has_new && wave == 0) {
+        // the new row rounded through fp8 into its ring slot.  Every workgroup
+        // whose list holds it writes the same bytes and gathers the slot only
+        // after its own write is complete (the wait below, then the barrier in
+        // pack), so each one reads its own write whatever L2 it sits behind.
+        const u32x4_t r = fp8_round_trip_chunk(new_raw);
+        if (C::CH == 64 || lane < C::CH)
+            *reinterpret_cast<u32x4_t *>(p.kv_ring + ((int64_t)bi * p.rows + p.new_slot) * D + lane * 8) = r;
+        asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+    }
+
     for (int c0 = lo; c0 < hi; c0 += kListCap) {
         const int c1 = min(hi, c0 + kListCap);
-        if (c0 != lo) cmp.load(idxq, c0, c1);
+        if (c0 != lo) cmp.load(fetch, c0, c1);
+        if (FUSED && hg == 0 && p.idx_out) cmp.store(p.idx_out + (int64_t)qi * p.topk, c0, c1);
         const int nv = cmp.pack(p.rows, list, wcnt);
         if (nv == 0) continue;
         const int nst = (nv + C::ROWS - 1) / C::ROWS;
@@ -432,45 +487,51 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
 // ------------------------------------------------------------------ decode --
 //
 // Decode kernel: one workgroup of four wavefronts per (query, group of 16
-// heads), for short index lists.  A stage covers 128 index entries; each
-// wavefront loads its 32 entries into registers and copies their rows straight
-// into LDS (a zero row for a -1 entry, which then contributes nothing), so no
-// list compaction sits on the latency path.  The wavefronts split the rows for
-// the scores (S^T[32 rows][16 heads] each, MFMA 16x16x32), exchange the
-// per-head maxima and the bf16 weights P through LDS, then split the head dim
-// for O^T[128 d][16 heads] = V^T P^T over all the stage's rows.  Every gathered
-// row is read from LDS once as K and once as V, and no partial result leaves
-// the workgroup.
+// heads), for decode-sized batches.  The query's 16 head rows are copied into
+// LDS once per workgroup (every wavefront needs all of them), and the index
+// list is walked in 64-entry stages two buffers deep, so the rows of stage t+1
+// arrive while stage t is computed.  Each wavefront copies the rows of its 16
+// entries of a stage straight from its index registers (a zero row for a -1
+// entry, which then contributes nothing), so no list compaction sits on the
+// latency path.  The wavefronts split the rows for the scores (S^T[16 rows][16
+// heads] each, MFMA 16x16x32), exchange the per-head maxima and the bf16
+// weights P through LDS, then split the head dim for O^T[d/4][16 heads] =
+// V^T P^T over all the stage's rows.  Every gathered row is read from LDS once
+// as K and once as V, and no partial result leaves the workgroup.
 template <int D>
 struct DecodeCfg {
     static constexpr int NW = 4;
     static constexpr int THREADS = 64 * NW;
-    static constexpr int ROWS = 32 * NW;          // rows per stage
+    static constexpr int HEADS = 16;
+    static constexpr int ROWS = 64;               // index entries per stage
+    static constexpr int RPW = ROWS / NW;         // entries (rows) each wavefront copies per stage
     static constexpr int ROW_BYTES = 2 * D;
     static constexpr int RS = ROW_BYTES + 48;     // padded LDS row stride (bank position 3 r + c)
-    static constexpr int CH = D / 8;
+    static constexpr int CH = D / 8;              // 16-byte chunks per row
     static constexpr int KS = D / 32;             // k-steps of the score product (16x16x32)
     static constexpr int DQ = D / NW;             // head-dim share of one wavefront in the weighted sum
     static constexpr int DT = DQ / 16;            // its 16-wide d tiles
-    static constexpr int RPW = ROWS / NW;         // rows each wavefront copies per stage
     static constexpr int PRS = 2 * ROWS + 16;     // padded row stride of the weight buffer P[head][row]
     static constexpr int STAGE_BYTES = ROWS * RS;
-    static_assert(KS >= 2 && DT >= 1 && RPW % 4 == 0, "tiling");
+    static constexpr int Q_BYTES = HEADS * RS;
+    static_assert(KS >= 2 && KS % 2 == 0 && DT >= 1 && RPW == 16, "tiling");
 };
 
-template <int D>
+template <int D, bool FUSED>
 __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
     using C = DecodeCfg<D>;
-    __shared__ __attribute__((aligned(1024))) char smem[C::STAGE_BYTES];
-    __shared__ __attribute__((aligned(16))) char pbuf[16 * C::PRS];
+    __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) char qbuf[C::Q_BYTES];
+    __shared__ __attribute__((aligned(16))) char pbuf[C::HEADS * C::PRS];
     __shared__ float smax[C::NW][16];
     __shared__ float ssum[C::NW][16];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave values in SGPRs
     const int lane = tid & 63;
     const int g = lane >> 4;  // 16-lane group: k (or m) block of a 16x16x32 operand
     const int n = lane & 15;  // head (B / C column) or row (A row)
+    const bool chunk_lane = C::CH == 64 || lane < C::CH;  // lanes that carry a 16-byte chunk of a row
 
     const uint32_t L = logical_wg((uint32_t)p.total_wg);
     const uint32_t sp = L % (uint32_t)p.n_sp;
@@ -481,80 +542,153 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
 
     const int lo = (int)sp * p.split_len;
     const int hi = min(p.topk, lo + p.split_len);
-    const int32_t *idxq = p.idx + (int64_t)qi * p.topk;
-    // this wave's 32 index entries of a stage sit in lanes 0..31 (mirrored in 32..63);
-    // the first stage's go in flight before anything else: they head the critical path
-    const int eoff = 32 * wave + (lane & 31);
-    int vnext = lo + eoff < hi ? idxq[lo + eoff] : -1;
+    const int nst = hi > lo ? (hi - lo + C::ROWS - 1) / C::ROWS : 0;
+    const int32_t *idxq = FUSED ? nullptr : p.idx + (int64_t)qi * p.topk;
+    auto fetch = [&](int e) -> int { return FUSED ? step_entry(p, qi, e) : idxq[e]; };
 
-    const int head = (int)hg * 16 + n;
-    const bool head_ok = head < p.h;
-    // Q as the B operand of the scores: lane (g, n) holds q[head n][32 ks + 8 g .. +8]
-    bf16x8_t qreg[C::KS];
-    {
-        const uint16_t *qrow = p.q + ((int64_t)qi * p.h + (head_ok ? head : 0)) * D + 8 * g;
+    // this wave's 16 entries of a stage sit in lanes 0..15 (mirrored in the other
+    // lane groups); the first three stages' go in flight before anything else
+    const int eoff = C::RPW * wave + (lane & 15);
+    auto fetch_stage = [&](int j) -> int {
+        const int e = lo + j * C::ROWS + eoff;
+        return e < hi ? fetch(e) : -1;
+    };
+    const int v0 = fetch_stage(0);
+    int v_up = fetch_stage(1);     // entries of the next stage to copy
+    int v_after = fetch_stage(2);  // and of the one after
+    // the entries are in registers before any copy goes out: a compiler-placed wait
+    // for them after the copies would also wait for the copies
+    asm volatile("" : : "v"(v0), "v"(v_up), "v"(v_after));
+
+    // fused step: the new row (list entry window - 1) is copied raw like any other
+    // row (from kv_new instead of the ring), then rounded through fp8 in LDS by the
+    // wavefront that copied it; head group 0 writes it into its ring slot at the end
+    const int e_new = FUSED ? p.window - 1 - lo : -1;  // offset in this range
+    const bool has_new = FUSED && e_new >= 0 && lo + e_new < hi;
+    const int st_new = has_new ? e_new / C::ROWS : -1;
+    const int w_new = has_new ? (e_new % C::ROWS) / C::RPW : -1;
+    const int u_new = has_new ? e_new % C::RPW : 0;
+
+    const uint16_t *kvb = p.kv + (int64_t)bi * p.rows * D;
+    const uint32_t smem_base = lds_addr((const SA_LDS void *)smem);
+    const uint32_t q_base = lds_addr((const SA_LDS void *)qbuf);
+    const SA_LDS char *lds = (const SA_LDS char *)smem;
+
+    // fused step, head group 0: the list written out
+    auto store_idx = [&](int j, int v) {
+        const int e = lo + j * C::ROWS + eoff;
+        if (FUSED && hg == 0 && p.idx_out && lane < 16 && e < hi) p.idx_out[(int64_t)qi * p.topk + e] = v;
+    };
+    // Copies of stage j into buffer j % 2: this wave's RPW rows, one wave
+    // instruction (one 16-byte chunk per lane of a row) each.  prep() takes the
+    // valid mask (bit u: row RPW wave + u) and puts row u's source address in lane
+    // u; copy_rows() sends rows [u0, u1).  A wave's memory instructions issue at the
+    // memory pipeline's pace, so the next stage's copies are spread over this
+    // stage's score product instead of holding the wave up in one block.
+    auto prep = [&](int j, int v, uint32_t &okm, uint64_t &src) {
+        const bool ok = v >= 0 && (int64_t)v < p.rows;
+        okm = (uint32_t)__ballot(ok) & 0xffffu;
+        const int u_src_new = (has_new && j == st_new && wave == w_new) ? u_new : -1;
+        src = (lane & 15) == u_src_new ? (uint64_t)(p.kv_new + (int64_t)qi * D)
+                                       : (uint64_t)(kvb + (int64_t)(ok ? v : 0) * D);
+    };
+    auto copy_rows = [&](int j, uint32_t okm, uint64_t src, int u0, int u1) {
+        const uint32_t buf = smem_base + (uint32_t)((j & 1) * C::STAGE_BYTES + wave * C::RPW * C::RS);
+        for (int u = u0; u < u1; ++u) {
+            if ((okm >> u) & 1) {
+                const uint64_t a = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((uint32_t)(src >> 32), u) << 32) |
+                                   (uint64_t)(uint32_t)__builtin_amdgcn_readlane((uint32_t)src, u);
+                if (chunk_lane) dma_16B(reinterpret_cast<const char *>(a) + 16 * lane, buf + u * C::RS);
+            } else if (chunk_lane) {
+                *reinterpret_cast<SA_LDS u32x4_t *>((SA_LDS char *)smem + (j & 1) * C::STAGE_BYTES +
+                                                    (wave * C::RPW + u) * C::RS + 16 * lane) = u32x4_t{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+
+    uint32_t okm_cur = 0, okm_nxt = 0;
+    uint64_t src_nxt = 0;
+    if (nst > 0) {
+        store_idx(0, v0);
+        // the query's head rows, once per workgroup: wavefront w copies heads 4w .. 4w+3
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks)
-            qreg[ks] = head_ok ? *reinterpret_cast<const bf16x8_t *>(qrow + 32 * ks) : bf16x8_t{};
+        for (int u = 0; u < 4; ++u) {
+            const int hl = 4 * wave + u;
+            const int head = (int)hg * C::HEADS + hl;
+            if (head < p.h) {
+                if (chunk_lane)
+                    dma_16B(p.q + ((int64_t)qi * p.h + head) * D + lane * 8,
+                            __builtin_amdgcn_readfirstlane(q_base + hl * C::RS));
+            } else if (chunk_lane) {
+                *reinterpret_cast<SA_LDS u32x4_t *>((SA_LDS char *)qbuf + hl * C::RS + 16 * lane) =
+                    u32x4_t{0u, 0u, 0u, 0u};
+            }
+        }
+        uint64_t src0;
+        prep(0, v0, okm_cur, src0);
+#pragma unroll 1
+        for (int u = 0; u < C::RPW; ++u) copy_rows(0, okm_cur, src0, u, u + 1);
     }
 
+    const int head = (int)hg * C::HEADS + n;
+    const bool head_ok = head < p.h;
+    bf16x8_t qreg[C::KS];
     float m_ref = -1e30f;  // reference max (log2 domain), identical in all four wavefronts
     float l_run = 0.0f;    // this lane's share of the running sum over this wave's rows
     f32x4_t acc_o[C::DT];
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) acc_o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    u32x4_t new_row = {0u, 0u, 0u, 0u};
+    constexpr int CPI = C::RPW / (C::KS / 2);  // next-stage copies per score iteration
 
-    const uint16_t *kvb = p.kv + (int64_t)bi * p.rows * D;
-    const uint32_t smem_base = lds_addr((const SA_LDS void *)smem);
-    const SA_LDS char *lds = (const SA_LDS char *)smem;
-    const SA_LDS char *pl = (const SA_LDS char *)pbuf;
-    // score operand: row 32 wave + 16 t + n, d chunk 4 ks + g
-    const SA_LDS char *kb = lds + (32 * wave + n) * C::RS + 16 * g;
-    // weighted-sum operand (transposing read): rows 32 ks + 8 g + 4 rd + p/4, d 16 dt + 4 (p%4) of this wave's quarter
-    const SA_LDS char *vb = lds + (8 * g + (n >> 2)) * C::RS + 2 * C::DQ * wave + 8 * (n & 3);
-
-    for (int ebase = lo; ebase < hi; ebase += C::ROWS) {
-        // ---- gather: valid entries (0 <= v < rows) are copied row by row straight
-        //      from the index registers; other slots get a zero row, which adds nothing ----
-        const int v = vnext;
-        const bool ok = v >= 0 && (int64_t)v < p.rows;
-        const uint64_t okm = __ballot(ok) & 0xffffffffull;   // bit r: row 32 wave + r valid
-        if (ebase + C::ROWS < hi) {                           // next stage's entries in flight
-            const int e = ebase + C::ROWS + eoff;
-            vnext = e < hi ? idxq[e] : -1;
+    for (int t = 0; t < nst; ++t) {
+        const int ebase = lo + t * C::ROWS;
+        const SA_LDS char *stage = lds + (t & 1) * C::STAGE_BYTES;
+        // ---- this wave's copies of stage t complete ----
+        asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+        if (FUSED && t == st_new && wave == w_new) {
+            // the raw new row has landed: round it through fp8 in place
+            SA_LDS u32x4_t *nr = reinterpret_cast<SA_LDS u32x4_t *>((SA_LDS char *)stage +
+                                                                      (wave * C::RPW + u_new) * C::RS + 16 * lane);
+            const u32x4_t raw = chunk_lane ? *nr : u32x4_t{0u, 0u, 0u, 0u};
+            new_row = fp8_round_trip_chunk(raw);
+            if (chunk_lane) *nr = new_row;
         }
+        lds_barrier();  // every wave's rows (and the head rows) in place; stage t-1 fully consumed
+        const bool more = t + 1 < nst;  // stage t+1 goes into the buffer stage t-1 used
+        if (more) {
+            store_idx(t + 1, v_up);
+            prep(t + 1, v_up, okm_nxt, src_nxt);
+        }
+        if (t == 0) {
+            // Q as the B operand of the scores: lane (g, n) holds q[head n][32 ks + 8 g .. +8]
 #pragma unroll
-        for (int u = 0; u < C::RPW; ++u) {
-            const uint32_t dst = smem_base + (wave * C::RPW + u) * C::RS;
-            if ((okm >> u) & 1) {
-                const int row = __builtin_amdgcn_readlane(v, u);
-                if (C::CH == 64 || lane < C::CH)
-                    dma_16B(kvb + (int64_t)row * D + lane * 8, __builtin_amdgcn_readfirstlane(dst));
-            } else if (C::CH == 64 || lane < C::CH) {
-                *reinterpret_cast<SA_LDS u32x4_t *>((SA_LDS char *)smem + (wave * C::RPW + u) * C::RS + 16 * lane) =
-                    u32x4_t{0u, 0u, 0u, 0u};
-            }
+            for (int ks = 0; ks < C::KS; ++ks)
+                qreg[ks] = lds_read_b128((const SA_LDS char *)qbuf + n * C::RS + 64 * ks + 16 * g);
         }
-        wait_all_barrier();  // copied and zeroed rows of every wave in place
 
-        // ---- scores S^T for this wave's 32 rows: two 16-row tiles ----
+        // ---- scores S^T for this wave's 16 rows: two accumulation chains ----
+        const SA_LDS char *kb = stage + (C::RPW * wave + n) * C::RS + 16 * g;
         f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
+        for (int ks = 0; ks < C::KS; ks += 2) {
             const bf16x8_t a0 = lds_read_b128(kb + 64 * ks);
-            const bf16x8_t a1 = lds_read_b128(kb + 16 * C::RS + 64 * ks);
+            const bf16x8_t a1 = lds_read_b128(kb + 64 * (ks + 1));
+            if (more) copy_rows(t + 1, okm_nxt, src_nxt, (ks / 2) * CPI, (ks / 2 + 1) * CPI);
             s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qreg[ks], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qreg[ks], s1, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qreg[ks + 1], s1, 0, 0, 0);
         }
-        // value i of tile t in lane (g, n): row 32 wave + 16 t + 4 g + i, head n
-        float sv[8];
+        if (more) {
+            v_up = v_after;
+            v_after = fetch_stage(t + 3);
+        }
+        // value i of lane (g, n): row RPW wave + 4 g + i, head n
+        float sv[4];
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int r = 4 * g + i;
-            sv[i] = (okm >> r) & 1 ? s0[i] * p.scale_log2 : -INFINITY;
-            sv[4 + i] = (okm >> (r + 16)) & 1 ? s1[i] * p.scale_log2 : -INFINITY;
-            mx = fmaxf(mx, fmaxf(sv[i], sv[4 + i]));
+            sv[i] = (okm_cur >> (4 * g + i)) & 1 ? (s0[i] + s1[i]) * p.scale_log2 : -INFINITY;
+            mx = fmaxf(mx, sv[i]);
         }
         mx = fmaxf(mx, shfl_xor_f32(mx, 16));
         mx = fmaxf(mx, shfl_xor_f32(mx, 32));
@@ -571,24 +705,25 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
             }
             m_ref = m_new;
         }
-        // weights -> bf16 -> P[head][row] in LDS (rows 32 wave + 16 t + 4 g + 0..3)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const uint32_t b0 = pack_bf16x2(exp2_fast(sv[4 * t] - m_ref), exp2_fast(sv[4 * t + 1] - m_ref));
-            const uint32_t b1 = pack_bf16x2(exp2_fast(sv[4 * t + 2] - m_ref), exp2_fast(sv[4 * t + 3] - m_ref));
+        // weights -> bf16 -> P[head][row] in LDS (rows RPW wave + 4 g + 0..3)
+        {
+            const uint32_t b0 = pack_bf16x2(exp2_fast(sv[0] - m_ref), exp2_fast(sv[1] - m_ref));
+            const uint32_t b1 = pack_bf16x2(exp2_fast(sv[2] - m_ref), exp2_fast(sv[3] - m_ref));
             l_run += __uint_as_float(b0 << 16) + __uint_as_float(b0 & 0xffff0000u) + __uint_as_float(b1 << 16) +
                      __uint_as_float(b1 & 0xffff0000u);
-            *reinterpret_cast<SA_LDS u32x2_t *>((SA_LDS char *)pl + n * C::PRS + 2 * (32 * wave + 16 * t + 4 * g)) =
+            *reinterpret_cast<SA_LDS u32x2_t *>((SA_LDS char *)pbuf + n * C::PRS + 2 * (C::RPW * wave + 4 * g)) =
                 u32x2_t{b0, b1};
         }
         lds_barrier();
 
         // ---- O^T[this wave's d quarter][16 heads] += V^T P^T over the stage's rows ----
-        const int nks = min(C::ROWS, hi - ebase + 31) / 32;  // 32-row k-steps holding entries
+        // (transposing read: rows 32 ks + 8 g + 4 rd + p/4, d 16 dt + 4 (p%4) of the quarter)
+        const SA_LDS char *vb = stage + (8 * g + (n >> 2)) * C::RS + 2 * C::DQ * wave + 8 * (n & 3);
 #pragma unroll
         for (int ks = 0; ks < C::ROWS / 32; ++ks) {
-            if (ks < nks) {
-                const bf16x8_t pb = lds_read_b128(pl + n * C::PRS + 2 * (32 * ks + 8 * g));
+            if (32 * ks < hi - ebase) {  // k-steps past the list end hold only zero weights
+                const bf16x8_t pb =
+                    lds_read_b128((const SA_LDS char *)pbuf + n * C::PRS + 2 * (32 * ks + 8 * g));
 #pragma unroll
                 for (int dt = 0; dt < C::DT; ++dt) {
                     const i16x4_t lo4 = lds_read_tr16(vb + (32 * ks) * C::RS + 32 * dt);
@@ -599,7 +734,7 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
                 }
             }
         }
-        lds_barrier();  // buffer and weights free for the next stage
+        okm_cur = okm_nxt;
     }
 
     // this wave's share of the sum: add the four lane groups, then the four waves
@@ -608,6 +743,9 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
     if (g == 0) ssum[wave][n] = l_run;
     lds_barrier();
     const float l_tot = (ssum[0][n] + ssum[1][n]) + (ssum[2][n] + ssum[3][n]);
+
+    if (FUSED && hg == 0 && has_new && wave == w_new && chunk_lane)
+        *reinterpret_cast<u32x4_t *>(p.kv_ring + ((int64_t)bi * p.rows + p.new_slot) * D + lane * 8) = new_row;
 
     if (p.n_sp > 1) {
         if (head_ok) {
@@ -740,15 +878,17 @@ sa_status resolve_variant(int64_t nq, int32_t h, int32_t topk, int32_t kernel, i
     return SA_OK;
 }
 
-template <int D>
+template <int D, bool FUSED>
 hipError_t launch_wide(const AttnParams &p, hipStream_t stream) {
-    hipLaunchKernelGGL((sa_attn_wide<D>), dim3((unsigned)p.total_wg), dim3(WideCfg<D>::THREADS), 0, stream, p);
+    hipLaunchKernelGGL((sa_attn_wide<D, FUSED>), dim3((unsigned)p.total_wg), dim3(WideCfg<D>::THREADS), 0, stream,
+                       p);
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool FUSED>
 hipError_t launch_decode(const AttnParams &p, hipStream_t stream) {
-    hipLaunchKernelGGL((sa_attn_decode<D>), dim3((unsigned)p.total_wg), dim3(DecodeCfg<D>::THREADS), 0, stream, p);
+    hipLaunchKernelGGL((sa_attn_decode<D, FUSED>), dim3((unsigned)p.total_wg), dim3(DecodeCfg<D>::THREADS), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
@@ -761,6 +901,76 @@ hipError_t launch_combine(const AttnParams &p, hipStream_t stream) {
 }
 
 bool valid_d(int32_t d) { return d == 64 || d == 128 || d == 256 || d == 512; }
+
+template <bool FUSED>
+hipError_t launch_attn(const AttnParams &p, const Variant &v, int32_t d, hipStream_t hs) {
+    if (v.kernel == SA_KERNEL_DECODE) {
+        switch (d) {
+            case 64: return launch_decode<64, FUSED>(p, hs);
+            case 128: return launch_decode<128, FUSED>(p, hs);
+            case 256: return launch_decode<256, FUSED>(p, hs);
+            default: return launch_decode<512, FUSED>(p, hs);
+        }
+    }
+    switch (d) {
+        case 64: return launch_wide<64, FUSED>(p, hs);
+        case 128: return launch_wide<128, FUSED>(p, hs);
+        case 256: return launch_wide<256, FUSED>(p, hs);
+        default: return launch_wide<512, FUSED>(p, hs);
+    }
+}
+
+hipError_t launch_combine_d(const AttnParams &p, int32_t d, hipStream_t hs) {
+    switch (d) {
+        case 64: return launch_combine<64>(p, hs);
+        case 128: return launch_combine<128>(p, hs);
+        case 256: return launch_combine<256>(p, hs);
+        default: return launch_combine<512>(p, hs);
+    }
+}
+
+// Parameters shared by the plain call and the fused decode step; the workspace
+// has been checked against the variant.
+AttnParams base_params(const uint16_t *q, const uint16_t *kv, const float *sink, int64_t nq, int64_t s, int32_t h,
+                       int32_t d, int64_t rows, int32_t topk, float scale, uint16_t *out, void *workspace,
+                       const Variant &v) {
+    AttnParams p = {};
+    p.q = q;
+    p.kv = kv;
+    p.sink = sink;
+    p.out = out;
+    const bool ws = v.n_sp > 1;
+    p.part_o = ws ? reinterpret_cast<float *>(workspace) : nullptr;
+    p.part_ml = ws ? reinterpret_cast<float *>(workspace) + (size_t)nq * v.n_sp * h * d : nullptr;
+    p.rows = rows;
+    p.nq = (int32_t)nq;
+    p.s = (int32_t)s;
+    p.h = h;
+    p.topk = topk;
+    p.n_hg = (h + v.heads_wg - 1) / v.heads_wg;
+    p.n_sp = v.n_sp;
+    p.split_len = v.split_len;
+    p.scale_log2 = scale * kLog2e;
+    return p;
+}
+
+template <bool FUSED>
+sa_status enqueue(AttnParams &p, const Variant &v, int32_t d, hipStream_t hs) {
+    const int64_t total = (int64_t)p.nq * p.n_hg * v.n_sp;
+    if (total > 0x7fffffffLL) return SA_ERR_SHAPE;
+    p.total_wg = (int32_t)total;
+    if (launch_attn<FUSED>(p, v, d, hs) != hipSuccess) return SA_ERR_HIP;
+    if (v.n_sp > 1 && launch_combine_d(p, d, hs) != hipSuccess) return SA_ERR_HIP;
+    return SA_OK;
+}
+
+sa_status check_workspace(const Variant &v, int64_t nq, int32_t h, int32_t d, void *workspace,
+                          size_t workspace_bytes) {
+    const size_t need = workspace_for(v, nq, h, d);
+    if (need > 0 && (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 16))
+        return SA_ERR_SHAPE;
+    return SA_OK;
+}
 
 sa_status run_sparse_attn(const uint16_t *q, const uint16_t *kv, const float *sink, const int32_t *idx,
                           int64_t b, int64_t s, int32_t h, int32_t d, int64_t rows, int32_t topk,
@@ -777,57 +987,45 @@ sa_status run_sparse_attn(const uint16_t *q, const uint16_t *kv, const float *si
     Variant v;
     sa_status st = resolve_variant(nq, h, topk, kernel, splits, &v);
     if (st != SA_OK) return st;
-    const size_t need = workspace_for(v, nq, h, d);
-    if (need > 0 && (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 16))
-        return SA_ERR_SHAPE;
-    AttnParams p;
-    p.q = q;
-    p.kv = kv;
-    p.sink = sink;
+    if ((st = check_workspace(v, nq, h, d, workspace, workspace_bytes)) != SA_OK) return st;
+    AttnParams p = base_params(q, kv, sink, nq, s, h, d, rows, topk, scale, out, workspace, v);
     p.idx = idx;
-    p.out = out;
-    p.part_o = need ? reinterpret_cast<float *>(workspace) : nullptr;
-    p.part_ml = need ? reinterpret_cast<float *>(workspace) + (size_t)nq * v.n_sp * h * d : nullptr;
-    p.rows = rows;
-    p.nq = (int32_t)nq;
-    p.s = (int32_t)s;
-    p.h = h;
-    p.topk = topk;
-    p.n_hg = (h + v.heads_wg - 1) / v.heads_wg;
-    p.n_sp = v.n_sp;
-    p.split_len = v.split_len;
-    p.scale_log2 = scale * kLog2e;
-    const int64_t total = nq * p.n_hg * v.n_sp;
-    if (total > 0x7fffffffLL) return SA_ERR_SHAPE;
-    p.total_wg = (int32_t)total;
-    hipStream_t hs = (hipStream_t)stream;
-    hipError_t e;
-    if (v.kernel == SA_KERNEL_DECODE) {
-        switch (d) {
-            case 64: e = launch_decode<64>(p, hs); break;
-            case 128: e = launch_decode<128>(p, hs); break;
-            case 256: e = launch_decode<256>(p, hs); break;
-            default: e = launch_decode<512>(p, hs); break;
-        }
-    } else {
-        switch (d) {
-            case 64: e = launch_wide<64>(p, hs); break;
-            case 128: e = launch_wide<128>(p, hs); break;
-            case 256: e = launch_wide<256>(p, hs); break;
-            default: e = launch_wide<512>(p, hs); break;
-        }
-    }
-    if (e != hipSuccess) return SA_ERR_HIP;
-    if (v.n_sp > 1) {
-        switch (d) {
-            case 64: e = launch_combine<64>(p, hs); break;
-            case 128: e = launch_combine<128>(p, hs); break;
-            case 256: e = launch_combine<256>(p, hs); break;
-            default: e = launch_combine<512>(p, hs); break;
-        }
-        if (e != hipSuccess) return SA_ERR_HIP;
-    }
-    return SA_OK;
+    return enqueue<false>(p, v, d, (hipStream_t)stream);
+}
+
+// Fused decode step: ring write of the new row (fp8 round trip), the window list,
+// the compressed append and the attention in one launch (plus the combine of a
+// split variant).
+sa_status run_decode_step(const uint16_t *q, uint16_t *kv, const uint16_t *kv_new, const float *sink,
+                          const int32_t *cidx, int32_t *idx_out, int64_t b, int32_t h, int32_t d, int64_t rows,
+                          int32_t window, int32_t kc, int64_t start_pos, float scale, uint16_t *out,
+                          void *workspace, size_t workspace_bytes, void *stream, int32_t kernel, int32_t splits) {
+    if (b < 0 || h < 0 || d < 0 || rows < 0 || window <= 0 || kc < 0 || start_pos < 0) return SA_ERR_SHAPE;
+    if (!valid_d(d)) return SA_ERR_UNSUPPORTED;
+    if (start_pos == 0) return SA_ERR_UNSUPPORTED;  // position 0 is a prefill
+    if (rows < window || rows > 0x7fffffffLL || b > 0x7fffffffLL) return SA_ERR_SHAPE;
+    if ((int64_t)window + kc > 0x7fffffffLL) return SA_ERR_SHAPE;
+    if (b == 0 || h == 0) return SA_OK;
+    if (!q || !kv || !kv_new || !sink || !out || (kc > 0 && !cidx)) return SA_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(kv) | reinterpret_cast<uintptr_t>(kv_new) |
+         reinterpret_cast<uintptr_t>(out)) % 16)
+        return SA_ERR_SHAPE;
+    const int32_t topk = window + kc;
+    Variant v;
+    sa_status st = resolve_variant(b, h, topk, kernel, splits, &v);
+    if (st != SA_OK) return st;
+    if ((st = check_workspace(v, b, h, d, workspace, workspace_bytes)) != SA_OK) return st;
+    AttnParams p = base_params(q, kv, sink, b, 1, h, d, rows, topk, scale, out, workspace, v);
+    p.kv_new = kv_new;
+    p.kv_ring = kv;
+    p.cidx = cidx;
+    p.idx_out = idx_out;
+    p.pos = start_pos;
+    p.window = window;
+    p.kc = kc;
+    p.wbase = (int32_t)((start_pos + 1) % window);
+    p.new_slot = (int32_t)(start_pos % window);
+    return enqueue<true>(p, v, d, (hipStream_t)stream);
 }
 
 }  // namespace
@@ -861,4 +1059,22 @@ extern "C" sa_status sa_sparse_attn_ex(const uint16_t *q, const uint16_t *kv, co
                                        size_t workspace_bytes, void *stream, int32_t kernel, int32_t splits) {
     return run_sparse_attn(q, kv, sink, idx, b, s, h, d, rows, topk, scale, out, workspace, workspace_bytes,
                            stream, kernel, splits);
+}
+
+extern "C" size_t sa_sparse_attn_decode_step_workspace_bytes(int64_t b, int32_t h, int32_t d, int32_t window,
+                                                             int32_t kc, int32_t kernel, int32_t splits) {
+    if (b < 0 || h <= 0 || window <= 0 || kc < 0 || !valid_d(d) || (int64_t)window + kc > 0x7fffffffLL) return 0;
+    Variant v;
+    if (resolve_variant(b, h, window + kc, kernel, splits, &v) != SA_OK) return 0;
+    return workspace_for(v, b, h, d);
+}
+
+extern "C" sa_status sa_sparse_attn_decode_step(const uint16_t *q, uint16_t *kv, const uint16_t *kv_new,
+                                                const float *sink, const int32_t *cidx, int32_t *idx_out,
+                                                int64_t b, int32_t h, int32_t d, int64_t rows, int32_t window,
+                                                int32_t kc, int64_t start_pos, float scale, uint16_t *out,
+                                                void *workspace, size_t workspace_bytes, void *stream,
+                                                int32_t kernel, int32_t splits) {
+    return run_decode_step(q, kv, kv_new, sink, cidx, idx_out, b, h, d, rows, window, kc, start_pos, scale, out,
+                           workspace, workspace_bytes, stream, kernel, splits);
 }

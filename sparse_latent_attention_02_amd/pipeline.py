@@ -9,6 +9,8 @@ A step is what one layer does per forward call on its attention inputs:
      window columns, shifted past the window rows (sa_append_compressed_idxs);
   4. sparse attention over the selected rows (sa_sparse_attn).
 Everything runs through the C ABI on the current stream; torch only allocates.
+A decode step can also run as one launch (``step_fused``): the same four steps
+inside the attention kernel.
 
 KV rows that exist before the step -- the ring contents at a decode step and
 the compressed cache -- are rounded through fp8 once in ``prepare``, as the cache
@@ -21,7 +23,7 @@ from types import SimpleNamespace
 import torch
 
 from . import sparse_attn, window_kv_update, window_topk_idxs, append_compressed_idxs, act_quant_fp8_
-from . import workspace_bytes
+from . import workspace_bytes, sparse_attn_decode_step, decode_step_workspace_bytes
 from .workloads import WORKLOADS
 
 
@@ -52,6 +54,8 @@ def prepare(wid: int, raw: dict, device: str = "cuda") -> SimpleNamespace:
         assert st.chunk is not None and st.chunk.is_contiguous()
         st.ring = torch.zeros((w.b, w.window, w.d), dtype=torch.bfloat16, device=device)
     nws = workspace_bytes(w.b, w.s, w.h, w.d, w.topk)
+    if w.start_pos > 0:
+        nws = max(nws, decode_step_workspace_bytes(w.b, w.h, w.d, w.window, w.n_comp))
     st.ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=device)
     return st
 
@@ -97,3 +101,15 @@ def ring_run(st: SimpleNamespace) -> dict:
         res[f"decode{pos}"] = sparse_attn(st.q_dec[i], ring, st.sink, idx, w.scale)
         res[f"ring{pos}"] = ring.clone()
     return res
+
+
+def step_fused(st: SimpleNamespace) -> torch.Tensor:
+    """Steps 1-4 of a decode step in one launch (sa_sparse_attn_decode_step): the
+    new row is rounded and written into the ring, the list is built inside the
+    kernel and also written to ``st.idx``."""
+    w = st.w
+    assert w.start_pos > 0, "the fused step is a decode step"
+    return sparse_attn_decode_step(st.q, st.kv, st.new_rows.view(w.b, w.d), st.sink, w.window, w.start_pos,
+                                   w.scale, cidx=st.comp.view(w.b, w.n_comp) if st.comp is not None else None,
+                                   out=st.out, idx_out=st.idx, workspace=st.ws)
+

@@ -54,3 +54,26 @@ def test_host_only_calls(lib):
     assert lib.sa_sparse_attn(None, None, None, None, 1, 1, 1, 96, 1, 1, 0.1, None, None, 0, None) == sa.SA_ERR_UNSUPPORTED
     assert lib.sa_sparse_attn(None, None, None, None, 0, 1, 1, 64, 1, 1, 0.1, None, None, 0, None) == sa.SA_OK
     assert lib.sa_sparse_attn_workspace_bytes(1, 1, 1, 96, 1) == 0
+
+
+def test_decode_step_argument_checks(lib):
+    import sparse_latent_attention_02_amd as sa
+    f = lib.sa_sparse_attn_decode_step
+    # (q, kv, kv_new, sink, cidx, idx_out, b, h, d, rows, window, kc, start_pos, scale, out, ws, ws_bytes, stream,
+    #  kernel, splits)
+    assert f(None, None, None, None, None, None, 2, 4, 64, 8, 8, 0, 0, 0.1, None, None, 0, None, 0, 0) == \
+        sa.SA_ERR_UNSUPPORTED                                   # position 0 is a prefill
+    assert f(None, None, None, None, None, None, 2, 4, 96, 8, 8, 0, 5, 0.1, None, None, 0, None, 0, 0) == \
+        sa.SA_ERR_UNSUPPORTED                                   # head dim
+    assert f(None, None, None, None, None, None, 2, 4, 64, 7, 8, 0, 5, 0.1, None, None, 0, None, 0, 0) == \
+        sa.SA_ERR_SHAPE                                         # ring longer than the buffer
+    assert f(None, None, None, None, None, None, 2, 4, 64, 8, 0, 0, 5, 0.1, None, None, 0, None, 0, 0) == \
+        sa.SA_ERR_SHAPE                                         # empty ring
+    assert f(None, None, None, None, None, None, 0, 4, 64, 8, 8, 0, 5, 0.1, None, None, 0, None, 0, 0) == sa.SA_OK
+    assert f(None, None, None, None, None, None, 2, 4, 64, 8, 8, 0, 5, 0.1, None, None, 0, None, 0, 0) == \
+        sa.SA_ERR_NULL
+    assert f(None, None, None, None, None, None, 2, 4, 64, 8, 8, 0, 5, 0.1, None, None, 0, None, 3, 0) in \
+        (sa.SA_ERR_NULL, sa.SA_ERR_UNSUPPORTED)
+    assert lib.sa_sparse_attn_decode_step_workspace_bytes(2, 4, 96, 8, 0, 0, 0) == 0
+    assert lib.sa_sparse_attn_decode_step_workspace_bytes(64, 64, 512, 128, 0, 0, 0) == 0
+    assert lib.sa_sparse_attn_decode_step_workspace_bytes(2, 64, 512, 128, 1024, 2, 4) == 2 * 4 * 64 * 514 * 4
