@@ -43,6 +43,7 @@
 #include "../../include/sparse_attn.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace {
 
@@ -50,7 +51,7 @@ using namespace sa;
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kListCap = 2048;        // compacted entries held in LDS at once
+constexpr int kListCap = 4096;        // compacted entries held in LDS at once
 constexpr float kRescaleSlack = 8.0f; // log2 units the reference max may lag behind
 
 struct AttnParams {
@@ -183,49 +184,62 @@ struct Compactor {
 
 template <int D>
 struct WideCfg {
-    // One wavefront holds 32 heads.  Up to d = 256 it covers the whole head dim;
-    // at d = 512 its Q (128 VGPRs) and O (256 accumulators) would not fit the
-    // register file, so a pair of wavefronts splits the head dim (DH = 2) and
-    // sums its partial scores through LDS before the softmax.
-    static constexpr int DH = D > 256 ? 2 : 1;
-    static constexpr int NW = 2 * DH;            // wavefronts: 2 head tiles x DH head-dim parts
+    // Four wavefronts: 2 head tiles of 32 heads x 2 row halves of every 64-row
+    // stage.  A wavefront covers the whole head dim of its 32 heads (Q in
+    // registers, O in accumulator registers) and keeps its own running max and
+    // sum over the rows it sees; the two row halves of a head tile are merged
+    // once, at the end (the algebra of the split combine).  A stage therefore
+    // needs no exchange between wavefronts and a single barrier.
+    static constexpr int NW = 4;
+    static constexpr int THREADS = 64 * NW;
     static constexpr int HEADS = 64;
-    static constexpr int DW = D / DH;            // head-dim slice of one wavefront
+    static constexpr int ROWS = 64;               // rows per stage (32 per wavefront)
+    static constexpr int RPW = ROWS / NW;         // rows each wavefront copies per stage
     static constexpr int ROW_BYTES = 2 * D;
     // LDS row stride: 3 spare 16-byte chunks per row put row r's chunk c at bank
     // position (3 r + c) mod 16, distinct for the 16 rows of an operand fetch and
     // for the 4 rows x 2 chunks of a transposing read -- and every operand
     // address is a per-lane base plus a compile-time offset
     static constexpr int RS = ROW_BYTES + 48;
-    static constexpr int CH = D / 8;             // 16-byte chunks per row
-    static constexpr int KS = DW / 16;           // k-steps of the score product
-    static constexpr int DT = DW / 32;           // 32-wide d tiles of the output
-    static constexpr int ROWS = 32;              // rows per stage
-    static constexpr int NBUF = DH > 1 ? 3 : 2;  // stage buffers: the copy runs NBUF-1 stages ahead
+    static constexpr int CH = D / 8;              // 16-byte chunks per row
+    static constexpr int KS = D / 16;             // k-steps of the score product
+    static constexpr int DT = D / 32;             // 32-wide d tiles of the output
     static constexpr int STAGE_BYTES = ROWS * RS;
-    static constexpr int RPW = ROWS / NW;        // rows each wavefront copies per stage
-    static constexpr int OUT_BYTES = HEADS * RS; // staged bf16 output of the workgroup
-    static constexpr int SMEM = NBUF * STAGE_BYTES > OUT_BYTES ? NBUF * STAGE_BYTES : OUT_BYTES;
-    static constexpr int XBYTES = DH > 1 ? NW * 64 * 64 : 16;  // partial-score exchange, 64 B per lane
-    static constexpr int THREADS = 64 * NW;
-    static_assert(RPW % 4 == 0 && KS >= 4 && DT >= 1, "tiling");
+    static constexpr int NBUF = 2;                // the copy of stage t+1 overlaps the maths of stage t
+    // operand reads in flight ahead of the MFMAs (score / weighted-sum product); at
+    // d = 512 Q and O fill the register file and the depth is kept small
+    // log2 units a stage max may exceed the fixed reference of the weights
+    static constexpr float SLACK = 32.0f;
+    static constexpr int PFK = D > 256 ? 2 : 4;
+    static constexpr int PFV = D > 256 ? 2 : 3;
+    // The next stage's copies are spread evenly over the KS MFMAs of the score
+    // product: a wave's memory instructions issue only as fast as the memory
+    // pipeline drains, and a wave held up issuing a block of them leaves its MFMA
+    // unit idle.  copy_at(i) = first copy issued at score step i.
+    static constexpr int copy_at(int i) { return (i * RPW + KS - 1) / KS; }
+    static constexpr int XO_BYTES = NW * (DT / 2) * 64 * 64;  // end merge: half the O tiles of every wave
+    static constexpr int OUT_BYTES = HEADS * RS;  // staged bf16 output of the workgroup
+    static constexpr int SMEM = std::max(NBUF * STAGE_BYTES, std::max(XO_BYTES, OUT_BYTES));
+    static_assert(KS >= 4 && DT >= 2 && DT % 2 == 0 && RPW == 16, "tiling");
 };
 
 template <int D, bool FUSED>
 __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const AttnParams p) {
     using C = WideCfg<D>;
     __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
-    __shared__ __attribute__((aligned(16))) char xbuf[C::XBYTES];
     __shared__ int list[kListCap];
     __shared__ int wcnt[kListCap / 64];
+    __shared__ float mlx[2][2][32][2];  // end merge: [head tile][row half][head][max, sum]
+    __shared__ int replay[2];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave values in SGPRs
     const int lane = tid & 63;
-    const int hf = lane >> 5;     // which half of a 32-wide MFMA k (or m) block this lane feeds
-    const int n = lane & 31;      // head (B / C column) or row (A row) of this lane
-    const int hw = wave / C::DH;  // head tile of this wavefront
-    const int dh = wave % C::DH;  // head-dim part of this wavefront
+    const int hf = lane >> 5;  // which half of a 32-wide MFMA k (or m) block this lane feeds
+    const int n = lane & 31;   // head (B / C column) or row (A row) of this lane
+    const int hw = wave >> 1;  // head tile of this wavefront
+    const int rh = wave & 1;   // row half of every stage this wavefront computes
+    const bool chunk_lane = C::CH == 64 || lane < C::CH;
 
     const uint32_t L = logical_wg((uint32_t)p.total_wg);
     const uint32_t sp = L % (uint32_t)p.n_sp;
@@ -241,7 +255,7 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
     // fused step: the new row's entry (window - 1) in this workgroup's range
     const bool has_new = FUSED && p.window - 1 >= lo && p.window - 1 < hi;
     u32x4_t new_raw = {0u, 0u, 0u, 0u};
-    if (has_new && wave == 0 && (C::CH == 64 || lane < C::CH))
+    if (has_new && wave == 0 && chunk_lane)
         new_raw = *reinterpret_cast<const u32x4_t *>(p.kv_new + (int64_t)qi * D + lane * 8);
     // the first index chunk goes in flight before anything else: it heads the critical path
     Compactor<C::THREADS> cmp;
@@ -249,30 +263,41 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
 
     const int head = ((int)hg * 2 + hw) * 32 + n;
     const bool head_ok = head < p.h;
+    const uint32_t smem_base = lds_addr((const SA_LDS void *)smem);
+    const SA_LDS char *lds = (const SA_LDS char *)smem;
 
-    // Q as the B operand: lane (hf, n) holds q[head n][slice + 16 ks + 8 hf .. +8] for every ks.
-    bf16x8_t qreg[C::KS];
-    {
-        const uint16_t *qrow = p.q + ((int64_t)qi * p.h + (head_ok ? head : 0)) * D + dh * C::DW + 8 * hf;
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks)
-            qreg[ks] = head_ok ? *reinterpret_cast<const bf16x8_t *>(qrow + 16 * ks) : bf16x8_t{};
+    // the workgroup's 64 head rows of q, copied once into stage buffer 0 (wave w
+    // copies rows 16 w .. 16 w + 15; heads past h get zero rows) and read into
+    // registers after the first compaction -- both wavefronts of a head tile need
+    // them, and a copy through LDS fetches them once.  Stage st then uses buffer
+    // (st + 1) % 2, so stage 0 does not overwrite them.
+#pragma unroll 1
+    for (int u = 0; u < C::RPW; ++u) {
+        const int hl = wave * C::RPW + u;
+        const int hd = (int)hg * C::HEADS + hl;
+        if (hd < p.h) {
+            if (chunk_lane) dma_16B(p.q + ((int64_t)qi * p.h + hd) * D + lane * 8, smem_base + hl * C::RS);
+        } else if (chunk_lane) {
+            *reinterpret_cast<SA_LDS u32x4_t *>((SA_LDS char *)smem + hl * C::RS + 16 * lane) =
+                u32x4_t{0u, 0u, 0u, 0u};
+        }
     }
+    // Q as the B operand: lane (hf, n) holds q[head n][16 ks + 8 hf .. +8] for every ks
+    bf16x8_t qreg[C::KS];
 
-    float m_ref = -1e30f;  // running max (log2 domain) the weights are taken against
-    float l_run = 0.0f;    // this lane's share of the running sum
+    float m_ref = -1e30f;   // fixed reference max (log2 domain) the weights are taken against
+    float m_seen = -1e30f;  // largest stage max seen
+    float l_run = 0.0f;     // this lane's share of the running sum
     f32x16_t acc_o[C::DT];
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) acc_o[dt] = f32x16_t{};
+    if (tid == 0) replay[0] = replay[1] = 0;  // read only after the barriers of pack
 
     const uint16_t *kvb = p.kv + (int64_t)bi * p.rows * D;
-    const uint32_t smem_base = lds_addr((const SA_LDS void *)smem);
-    const SA_LDS char *lds = (const SA_LDS char *)smem;
     // per-lane operand bases inside a stage buffer (see the two read patterns below)
-    const int slice = 2 * dh * C::DW;  // byte offset of this wave's head-dim slice in a row
-    const int koff = n * C::RS + slice + 16 * hf;
+    const int koff = (32 * rh + n) * C::RS + 16 * hf;
     const int p16 = lane & 15;
-    const int voff = (4 * hf + (p16 >> 2)) * C::RS + slice + 16 * (2 * ((lane >> 4) & 1) + ((p16 & 3) >> 1)) +
+    const int voff = (32 * rh + 4 * hf + (p16 >> 2)) * C::RS + 16 * (2 * ((lane >> 4) & 1) + ((p16 & 3) >> 1)) +
                      ((p16 & 1) << 3);
 
     if (has_new && wave == 0) {
@@ -281,60 +306,74 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
         // after its own write is complete (the wait below, then the barrier in
         // pack), so each one reads its own write whatever L2 it sits behind.
         const u32x4_t r = fp8_round_trip_chunk(new_raw);
-        if (C::CH == 64 || lane < C::CH)
+        if (chunk_lane)
             *reinterpret_cast<u32x4_t *>(p.kv_ring + ((int64_t)bi * p.rows + p.new_slot) * D + lane * 8) = r;
-        asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
     }
+    // this wave's copies of the head rows (and the ring write) complete; the
+    // barriers of the first compaction then publish every wave's
+    asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
 
+    // The weights are taken against a fixed reference: the first stage max a wave
+    // sees.  A later stage max may exceed it by up to SLACK (weights <= 2^SLACK, far
+    // inside bf16 and f32 range), so O is never rescaled inside the loop (with O
+    // and Q filling the register file there is no room to).  Should a stage max
+    // outrun the reference by more, the workgroup replays the whole list against
+    // the larger max -- correct for any input, and it does not occur for attention
+    // logits of any realistic spread.  replay[st & 1] is raised during stage st and
+    // read after the barrier that opens stage st+1; the two slots alternate, so a
+    // read never races the next stage's writes.
+    bool first_pass = true;
+    for (bool again = true; again; first_pass = false) {
+    again = false;
     for (int c0 = lo; c0 < hi; c0 += kListCap) {
         const int c1 = min(hi, c0 + kListCap);
-        if (c0 != lo) cmp.load(fetch, c0, c1);
-        if (FUSED && hg == 0 && p.idx_out) cmp.store(p.idx_out + (int64_t)qi * p.topk, c0, c1);
+        if (c0 != lo || !first_pass) cmp.load(fetch, c0, c1);
+        if (FUSED && first_pass && hg == 0 && p.idx_out) cmp.store(p.idx_out + (int64_t)qi * p.topk, c0, c1);
         const int nv = cmp.pack(p.rows, list, wcnt);
+        if (c0 == lo && first_pass) {
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ++ks)
+                qreg[ks] = lds_read_b128(lds + (hw * 32 + n) * C::RS + 32 * ks + 16 * hf);
+        }
         if (nv == 0) continue;
         const int nst = (nv + C::ROWS - 1) / C::ROWS;
-        const int last_row = list[nv - 1];
 
-        // copies of one stage: this wave's RPW rows, one wave instruction (one row) each;
-        // the list entries are read in one go, entries past the end repeat the last valid row
-        auto issue = [&](int st) {
-            const uint32_t buf = smem_base + (uint32_t)((st % C::NBUF) * C::STAGE_BYTES);
-            const int e0 = st * C::ROWS + wave * C::RPW;
-            int rowv[C::RPW];
-#pragma unroll
-            for (int u = 0; u < C::RPW; u += 4) {
-                const i32x4_t r4 = *reinterpret_cast<const SA_LDS i32x4_t *>((const SA_LDS int *)list + e0 + u);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) rowv[u + c] = e0 + u + c < nv ? r4[c] : last_row;
-            }
-#pragma unroll
-            for (int u = 0; u < C::RPW; ++u) {
-                const int r = wave * C::RPW + u;
-                if (C::CH == 64 || lane < C::CH)
-                    dma_16B(kvb + (int64_t)rowv[u] * D + lane * 8, __builtin_amdgcn_readfirstlane(buf + r * C::RS));
+        // copies of stage st into buffer (st + 1) % 2: this wave's RPW rows, one wave
+        // instruction (one 16-byte chunk per lane of a row) each.  Lane u (< RPW)
+        // holds the row of copy u; entries past the list end repeat its last row.
+        auto stage_rows = [&](int st) -> int {
+            const int e = st * C::ROWS + wave * C::RPW + (lane & 15);
+            return list[e < nv ? e : nv - 1];
+        };
+        auto copy_rows = [&](int st, int rows_reg, int u0, int u1) {
+            const uint32_t buf = smem_base + (uint32_t)(((st + 1) & 1) * C::STAGE_BYTES + wave * C::RPW * C::RS);
+            for (int u = u0; u < u1; ++u) {
+                const int row = __builtin_amdgcn_readlane(rows_reg, u);
+                if (chunk_lane) dma_16B(kvb + (int64_t)row * D + lane * 8, buf + u * C::RS);
             }
         };
+        {
+            const int r0 = stage_rows(0);
+#pragma unroll 1
+            for (int u = 0; u < C::RPW; ++u) copy_rows(0, r0, u, u + 1);
+        }
 
-        issue(0);
-        if (C::NBUF > 2 && nst > 1) issue(1);
         for (int st = 0; st < nst; ++st) {
-            if (st + C::NBUF - 1 < nst) {
-                issue(st + C::NBUF - 1);
-                wait_vmcnt_barrier<(C::NBUF - 1) * C::RPW>();
-            } else if (C::NBUF > 2 && st + 1 < nst) {
-                wait_vmcnt_barrier<C::RPW>();
-            } else {
-                wait_vmcnt_barrier<0>();
-            }
-            const SA_LDS char *buf = lds + (st % C::NBUF) * C::STAGE_BYTES;
+            asm volatile("s_waitcnt vmcnt(0)" : : : "memory");  // this wave's copies of stage st
+            lds_barrier();  // everyone's copies in place; stage st-1 consumed, its buffer free
+            if (st > 0 && replay[(st - 1) & 1]) break;          // (no copy in flight here)
+            const SA_LDS char *buf = lds + ((st + 1) & 1) * C::STAGE_BYTES;
+            const bool more = st + 1 < nst;
+            const int rows_next = more ? stage_rows(st + 1) : 0;
 
-            // ---- 3. scores: lane (hf, n) feeds row n, d chunk 2 ks + hf.  Operand reads
-            //      run four MFMAs ahead; the scheduling barriers keep the compiler from
-            //      hoisting all of them (which would spill the accumulators) ----
+            // ---- scores S^T[32 rows][32 heads]: lane (hf, n) feeds row n, d chunk 2 ks + hf.
+            //      Operand reads run four MFMAs ahead; the next stage's copies go out one
+            //      or a few per k-step, so the wave is not held up issuing them in a block;
+            //      the scheduling barriers keep the compiler from hoisting the reads ----
             f32x16_t sacc = {};
             {
                 const SA_LDS char *kb = buf + koff;
-                constexpr int PF = 4;
+                constexpr int PF = C::PFK;
                 bf16x8_t kq[PF];
 #pragma unroll
                 for (int i = 0; i < PF; ++i) kq[i] = lds_read_b128(kb + 32 * i);
@@ -342,34 +381,18 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
                 for (int ks = 0; ks < C::KS; ++ks) {
                     const bf16x8_t a = kq[ks % PF];
                     if (ks + PF < C::KS) kq[ks % PF] = lds_read_b128(kb + 32 * (ks + PF));
+                    if (more) copy_rows(st + 1, rows_next, C::copy_at(ks), C::copy_at(ks + 1));
                     sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc, 0, 0, 0);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
 
-            if (C::DH > 1) {
-                // the pair's partial scores over its two head-dim halves: each wave adds
-                // the other's, so both hold the same full-dim sums (f32 addition commutes)
-                SA_LDS char *xb = (SA_LDS char *)xbuf;
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<SA_LDS f32x4_t *>(xb + ((wave * 4 + j) * 64 + lane) * 16) =
-                        f32x4_t{sacc[4 * j], sacc[4 * j + 1], sacc[4 * j + 2], sacc[4 * j + 3]};
-                lds_barrier();
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const f32x4_t o =
-                        *reinterpret_cast<const SA_LDS f32x4_t *>(xb + (((wave ^ 1) * 4 + j) * 64 + lane) * 16);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) sacc[4 * j + e] += o[e];
-                }
-            }
-
-            // ---- 4. softmax: value i of lane (hf, n) is row 8(i/4) + 4 hf + i%4, head n ----
-            const int ebase = st * C::ROWS;
-            float sv[16];
+            // ---- softmax: value i of lane (hf, n) is row 8(i/4) + 4 hf + i%4 of this
+            //      wave's half, head n ----
+            const int ebase = st * C::ROWS + 32 * rh;
+            f32x16_t &sv = sacc;  // scores in the base-2 domain, in place
             float mx = -INFINITY;
-            if (ebase + C::ROWS <= nv) {
+            if (ebase + 32 <= nv) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     sv[i] = sacc[i] * p.scale_log2;
@@ -384,15 +407,10 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
                 }
             }
             mx = fmaxf(mx, shfl_xor_f32(mx, 32));
-            if (__ballot(mx > m_ref + kRescaleSlack)) {
-                const float m_new = fmaxf(m_ref, mx);
-                if (__ballot(m_ref > -1e29f)) {
-                    const float alpha = exp2_fast(m_ref - m_new);
-#pragma unroll
-                    for (int dt = 0; dt < C::DT; ++dt) acc_o[dt] *= alpha;
-                    l_run *= alpha;
-                }
-                m_ref = m_new;
+            m_seen = fmaxf(m_seen, mx);
+            if (__ballot(mx > m_ref + C::SLACK)) {
+                if (__ballot(m_ref > -1e29f) && lane == 0) replay[st & 1] = 1;
+                m_ref = m_seen;
             }
             uint32_t pk[8];
 #pragma unroll
@@ -404,9 +422,9 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
             const bf16x8_t pb0 = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
             const bf16x8_t pb1 = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[4], pk[5], pk[6], pk[7]});
 
-            // ---- 5. O^T += V^T P^T.  MFMA j = kk DT + dt; for it, the 16-lane group
-            //      (hf, column half) reads rows 16 kk + 8 rd + 4 hf + p/4 (rd = 0, 1),
-            //      columns 32 dt + 16 (column half) + 4 (p%4), p = lane % 16 ----
+            // ---- O^T += V^T P^T.  MFMA j = kk DT + dt; for it, the 16-lane group
+            //      (hf, column half) reads rows 16 kk + 8 rd + 4 hf + p/4 (rd = 0, 1) of this
+            //      wave's half, columns 32 dt + 16 (column half) + 4 (p%4), p = lane % 16 ----
             {
                 const SA_LDS char *vb = buf + voff;
                 auto vread = [&](int j) {
@@ -416,7 +434,7 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
                     return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
                 };
                 constexpr int NJ = 2 * C::DT;
-                constexpr int PF = 3;
+                constexpr int PF = C::PFV;
                 bf16x8_t vq[PF];
 #pragma unroll
                 for (int i = 0; i < PF; ++i) vq[i] = vread(i);
@@ -429,55 +447,120 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            lds_barrier();  // every wave is done with this buffer and the exchange slots
+        }
+        lds_barrier();  // the last stage's flag is raised by now
+        if (replay[0] | replay[1]) {
+            again = true;
+            break;
         }
     }
-
-    // full running sum of the head: add the other half's share
-    l_run += shfl_xor_f32(l_run, 32);
-
-    if (p.n_sp > 1) {
-        // ---- 6b. split partials: unnormalised O, running max and sum, no sink ----
-        if (head_ok) {
-            const int64_t prow = ((int64_t)qi * p.n_sp + sp) * p.h + head;
-            float *po = p.part_o + prow * D + dh * C::DW + 4 * hf;
+    if (again) {
+        // start over against the larger reference (replay[] read by every wave above)
+        lds_barrier();
+        if (tid == 0) replay[0] = replay[1] = 0;
 #pragma unroll
-            for (int dt = 0; dt < C::DT; ++dt)
+        for (int dt = 0; dt < C::DT; ++dt) acc_o[dt] = f32x16_t{};
+        l_run = 0.0f;
+    }
+    }
+
+    // ---- merge the two row halves of each head tile: M = max, O and l rescaled
+    //      to M and added.  Wave rh finalises d tiles [rh DT/2, (rh+1) DT/2) and
+    //      hands the other half of its O to its partner ----
+    l_run += shfl_xor_f32(l_run, 32);  // the head's sum over this wave's rows
+    lds_barrier();                     // stage buffers free
+    if (hf == 0) {
+        mlx[hw][rh][n][0] = m_ref;
+        mlx[hw][rh][n][1] = l_run;
+    }
+    lds_barrier();
+    const float m_o = mlx[hw][rh ^ 1][n][0];
+    const float l_o = mlx[hw][rh ^ 1][n][1];
+    const float M = fmaxf(m_ref, m_o);
+    const float f_s = exp2_fast(m_ref - M);
+    const float f_o = exp2_fast(m_o - M);
+    const float Ls = l_run * f_s + l_o * f_o;
+    constexpr int DH2 = C::DT / 2;
+    const bool split = p.n_sp > 1;
+    // output = (own O f_s + partner's O f_o) / (Ls + sink term); split partials
+    // keep O unnormalised against M
+    float a_s = f_s, a_o = f_o;
+    if (!split) {
+        const float sink_l2 = head_ok ? p.sink[head] * kLog2e : 0.f;
+        const float Lt = Ls + exp2_fast(sink_l2 - M);
+        const float inv = Lt > 0.f ? 1.0f / Lt : 0.f;  // empty list: 0 / inf, or a guarded 0 / 0
+        a_s *= inv;
+        a_o *= inv;
+    }
+    SA_LDS char *xo = (SA_LDS char *)smem;
+    // the row half R finalises d tiles [R DT/2, (R+1) DT/2) (a template parameter:
+    // register arrays take compile-time indices only)
+    auto finish = [&](auto RC) {
+        constexpr int R = decltype(RC)::value;
 #pragma unroll
-                for (int qd = 0; qd < 4; ++qd)
-                    *reinterpret_cast<f32x4_t *>(po + 32 * dt + 8 * qd) =
-                        f32x4_t{acc_o[dt][4 * qd], acc_o[dt][4 * qd + 1], acc_o[dt][4 * qd + 2],
-                                acc_o[dt][4 * qd + 3]};
-            if (hf == 0 && dh == 0) {
-                p.part_ml[prow * 2] = m_ref;
-                p.part_ml[prow * 2 + 1] = l_run;
+        for (int k = 0; k < DH2; ++k) {  // the partner's half, as it stands
+            const f32x16_t &v = acc_o[(1 - R) * DH2 + k];
+            SA_LDS f32x4_t *dst = reinterpret_cast<SA_LDS f32x4_t *>(xo + ((wave * DH2 + k) * 64 + lane) * 64);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) dst[q4] = f32x4_t{v[4 * q4], v[4 * q4 + 1], v[4 * q4 + 2], v[4 * q4 + 3]};
+        }
+        lds_barrier();
+#pragma unroll
+        for (int k = 0; k < DH2; ++k) {  // own half: own a_s + partner's a_o, in place
+            const SA_LDS f32x4_t *src =
+                reinterpret_cast<const SA_LDS f32x4_t *>(xo + (((wave ^ 1) * DH2 + k) * 64 + lane) * 64);
+            f32x16_t &w = acc_o[R * DH2 + k];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4_t x = src[q4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[4 * q4 + e] = fmaf(w[4 * q4 + e], a_s, x[e] * a_o);
             }
         }
-        return;
-    }
-
-    // ---- 6. sink fold + normalise, stage bf16 rows in LDS, store a row per instruction ----
-    {
-        const float sink_l2 = head_ok ? p.sink[head] * kLog2e : 0.f;
-        const float Lt = l_run + exp2_fast(sink_l2 - m_ref);
-        const float inv = Lt > 0.f ? 1.0f / Lt : 0.f;  // empty list: 0 / inf, or a guarded 0 / 0
-        // lane (hf, n) holds head n, d = 32 dt + 8 qd + 4 hf + (0..3)
-        SA_LDS char *orow = (SA_LDS char *)smem + (hw * 32 + n) * C::RS + slice + 8 * hf;
+        if (split) {
+            // ---- split partials: unnormalised O, running max and sum, no sink ----
+            if (head_ok) {
+                const int64_t prow = ((int64_t)qi * p.n_sp + sp) * p.h + head;
+                float *po = p.part_o + prow * D + 4 * hf;
 #pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt)
+                for (int k = 0; k < DH2; ++k)
+#pragma unroll
+                    for (int qd = 0; qd < 4; ++qd) {
+                        const f32x16_t &o = acc_o[R * DH2 + k];
+                        *reinterpret_cast<f32x4_t *>(po + 32 * (R * DH2 + k) + 8 * qd) =
+                            f32x4_t{o[4 * qd], o[4 * qd + 1], o[4 * qd + 2], o[4 * qd + 3]};
+                    }
+                if (hf == 0 && R == 0) {
+                    p.part_ml[prow * 2] = M;
+                    p.part_ml[prow * 2 + 1] = Ls;
+                }
+            }
+            return;
+        }
+        // ---- bf16 rows staged in LDS (over the merge area: after every wave's reads) ----
+        lds_barrier();
+        // lane (hf, n) holds head n, d = 32 dt + 8 qd + 4 hf + (0..3)
+        SA_LDS char *orow = (SA_LDS char *)smem + (hw * 32 + n) * C::RS + 8 * hf;
+#pragma unroll
+        for (int k = 0; k < DH2; ++k)
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd) {
-                const u32x2_t w = {pack_bf16x2(acc_o[dt][4 * qd] * inv, acc_o[dt][4 * qd + 1] * inv),
-                                   pack_bf16x2(acc_o[dt][4 * qd + 2] * inv, acc_o[dt][4 * qd + 3] * inv)};
-                *reinterpret_cast<SA_LDS u32x2_t *>(orow + 64 * dt + 16 * qd) = w;
+                const f32x16_t &o = acc_o[R * DH2 + k];
+                const u32x2_t w = {pack_bf16x2(o[4 * qd], o[4 * qd + 1]), pack_bf16x2(o[4 * qd + 2], o[4 * qd + 3])};
+                *reinterpret_cast<SA_LDS u32x2_t *>(orow + 64 * (R * DH2 + k) + 16 * qd) = w;
             }
-    }
+    };
+    if (rh == 0)
+        finish(std::integral_constant<int, 0>{});
+    else
+        finish(std::integral_constant<int, 1>{});
+    if (split) return;
     lds_barrier();
     // one head row per wave instruction: lane l stores chunk l (16 B) of the row
 #pragma unroll 4
     for (int hr = wave; hr < C::HEADS; hr += C::NW) {
         const int hglob = (int)hg * C::HEADS + hr;
-        if (hglob < p.h && (C::CH == 64 || lane < C::CH)) {
+        if (hglob < p.h && chunk_lane) {
             const u32x4_t v = *reinterpret_cast<const SA_LDS u32x4_t *>(lds + hr * C::RS + 16 * lane);
             *reinterpret_cast<u32x4_t *>(p.out + ((int64_t)qi * p.h + hglob) * D + lane * 8) = v;
         }
