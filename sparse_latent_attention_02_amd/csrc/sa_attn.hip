@@ -141,6 +141,13 @@ struct Compactor {
         }
     }
 
+    // wait for the entry loads here: a compiler-placed wait for them further on
+    // would also wait for every copy queued behind them
+    __device__ __forceinline__ void ready() const {
+#pragma unroll
+        for (int k = 0; k < K; ++k) asm volatile("" : : "v"(v[k]));
+    }
+
     // the raw entries of [c0, c1) written out (fused decode step, one head group)
     __device__ __forceinline__ void store(int32_t *out, int c0, int c1) const {
 #pragma unroll
@@ -217,9 +224,13 @@ struct WideCfg {
     // pipeline drains, and a wave held up issuing a block of them leaves its MFMA
     // unit idle.  copy_at(i) = first copy issued at score step i.
     static constexpr int copy_at(int i) { return (i * RPW + KS - 1) / KS; }
-    static constexpr int XO_BYTES = NW * (DT / 2) * 64 * 64;  // end merge: half the O tiles of every wave
+    // end merge: each wavefront hands half its O tiles (DT/2) to its partner in NR
+    // rounds of TPR tiles, 64 B per lane per tile, next to the staged bf16 output
+    static constexpr int NR = DT / 2 > 1 ? 2 : 1;
+    static constexpr int TPR = DT / 2 / NR;
+    static constexpr int XR_BYTES = NW * TPR * 64 * 64;
     static constexpr int OUT_BYTES = HEADS * RS;  // staged bf16 output of the workgroup
-    static constexpr int SMEM = std::max(NBUF * STAGE_BYTES, std::max(XO_BYTES, OUT_BYTES));
+    static constexpr int SMEM = std::max(NBUF * STAGE_BYTES, XR_BYTES + OUT_BYTES);
     static_assert(KS >= 4 && DT >= 2 && DT % 2 == 0 && RPW == 16, "tiling");
 };
 
@@ -261,6 +272,18 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
     Compactor<C::THREADS> cmp;
     cmp.load(fetch, lo, min(hi, lo + kListCap));
 
+    cmp.ready();
+    if (has_new && wave == 0) {
+        // the new row rounded through fp8 into its ring slot.  Every workgroup
+        // whose list holds it writes the same bytes and gathers the slot only
+        // after its own write is complete (the wait below, then the barrier in
+        // pack), so each one reads its own write whatever L2 it sits behind.
+        const u32x4_t r = fp8_round_trip_chunk(new_raw);
+        if (chunk_lane)
+            *reinterpret_cast<u32x4_t *>(p.kv_ring + ((int64_t)bi * p.rows + p.new_slot) * D + lane * 8) = r;
+        asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+    }
+
     const int head = ((int)hg * 2 + hw) * 32 + n;
     const bool head_ok = head < p.h;
     const uint32_t smem_base = lds_addr((const SA_LDS void *)smem);
@@ -268,9 +291,9 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
 
     // the workgroup's 64 head rows of q, copied once into stage buffer 0 (wave w
     // copies rows 16 w .. 16 w + 15; heads past h get zero rows) and read into
-    // registers after the first compaction -- both wavefronts of a head tile need
-    // them, and a copy through LDS fetches them once.  Stage st then uses buffer
-    // (st + 1) % 2, so stage 0 does not overwrite them.
+    // registers once the first stage's copies are out -- both wavefronts of a head
+    // tile need them, and a copy through LDS fetches them once.  Stage st uses
+    // buffer (st + 1) % 2, so stage 0 does not overwrite them.
 #pragma unroll 1
     for (int u = 0; u < C::RPW; ++u) {
         const int hl = wave * C::RPW + u;
@@ -300,18 +323,6 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
     const int voff = (32 * rh + 4 * hf + (p16 >> 2)) * C::RS + 16 * (2 * ((lane >> 4) & 1) + ((p16 & 3) >> 1)) +
                      ((p16 & 1) << 3);
 
-    if (has_new && wave == 0) {
-        // the new row rounded through fp8 into its ring slot.  Every workgroup
-        // whose list holds it writes the same bytes and gathers the slot only
-        // after its own write is complete (the wait below, then the barrier in
-        // pack), so each one reads its own write whatever L2 it sits behind.
-        const u32x4_t r = fp8_round_trip_chunk(new_raw);
-        if (chunk_lane)
-            *reinterpret_cast<u32x4_t *>(p.kv_ring + ((int64_t)bi * p.rows + p.new_slot) * D + lane * 8) = r;
-    }
-    // this wave's copies of the head rows (and the ring write) complete; the
-    // barriers of the first compaction then publish every wave's
-    asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
 
     // The weights are taken against a fixed reference: the first stage max a wave
     // sees.  A later stage max may exceed it by up to SLACK (weights <= 2^SLACK, far
@@ -330,12 +341,6 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
         if (c0 != lo || !first_pass) cmp.load(fetch, c0, c1);
         if (FUSED && first_pass && hg == 0 && p.idx_out) cmp.store(p.idx_out + (int64_t)qi * p.topk, c0, c1);
         const int nv = cmp.pack(p.rows, list, wcnt);
-        if (c0 == lo && first_pass) {
-#pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks)
-                qreg[ks] = lds_read_b128(lds + (hw * 32 + n) * C::RS + 32 * ks + 16 * hf);
-        }
-        if (nv == 0) continue;
         const int nst = (nv + C::ROWS - 1) / C::ROWS;
 
         // copies of stage st into buffer (st + 1) % 2: this wave's RPW rows, one wave
@@ -352,11 +357,24 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
                 if (chunk_lane) dma_16B(kvb + (int64_t)row * D + lane * 8, buf + u * C::RS);
             }
         };
-        {
+        if (nv > 0) {
             const int r0 = stage_rows(0);
 #pragma unroll 1
             for (int u = 0; u < C::RPW; ++u) copy_rows(0, r0, u, u + 1);
         }
+        if (c0 == lo && first_pass) {
+            // this wave's head-row copies are done (only stage 0's RPW copies may still
+            // run); after the barrier, every wave's
+            if (nv > 0)
+                asm volatile("s_waitcnt vmcnt(%0)" : : "n"(C::RPW) : "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+            lds_barrier();
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ++ks)
+                qreg[ks] = lds_read_b128(lds + (hw * 32 + n) * C::RS + 32 * ks + 16 * hf);
+        }
+        if (nv == 0) continue;
 
         for (int st = 0; st < nst; ++st) {
             asm volatile("s_waitcnt vmcnt(0)" : : : "memory");  // this wave's copies of stage st
@@ -468,6 +486,7 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
     //      to M and added.  Wave rh finalises d tiles [rh DT/2, (rh+1) DT/2) and
     //      hands the other half of its O to its partner ----
     l_run += shfl_xor_f32(l_run, 32);  // the head's sum over this wave's rows
+    asm volatile("s_waitcnt vmcnt(0)" : : : "memory");  // (an empty list leaves the head-row copies running)
     lds_barrier();                     // stage buffers free
     if (hf == 0) {
         mlx[hw][rh][n][0] = m_ref;
@@ -493,75 +512,71 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
         a_o *= inv;
     }
     SA_LDS char *xo = (SA_LDS char *)smem;
-    // the row half R finalises d tiles [R DT/2, (R+1) DT/2) (a template parameter:
-    // register arrays take compile-time indices only)
+    SA_LDS char *stg = (SA_LDS char *)smem + C::XR_BYTES;  // staged bf16 output, clear of the exchange
+    // The row half R finalises d tiles [R DT/2, (R+1) DT/2) (a template parameter:
+    // register arrays take compile-time indices only).  The partner's share comes
+    // through LDS in NR rounds of TPR tiles; each merged tile goes straight to its
+    // destination (bf16 staging rows, or the split partials).
     auto finish = [&](auto RC) {
         constexpr int R = decltype(RC)::value;
 #pragma unroll
-        for (int k = 0; k < DH2; ++k) {  // the partner's half, as it stands
-            const f32x16_t &v = acc_o[(1 - R) * DH2 + k];
-            SA_LDS f32x4_t *dst = reinterpret_cast<SA_LDS f32x4_t *>(xo + ((wave * DH2 + k) * 64 + lane) * 64);
+        for (int r = 0; r < C::NR; ++r) {
+            if (r > 0) lds_barrier();  // the previous round's exchange has been read
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) dst[q4] = f32x4_t{v[4 * q4], v[4 * q4 + 1], v[4 * q4 + 2], v[4 * q4 + 3]};
-        }
-        lds_barrier();
+            for (int t = 0; t < C::TPR; ++t) {  // the partner's tiles of this round, as they stand
+                const f32x16_t &v = acc_o[(1 - R) * DH2 + r * C::TPR + t];
+                // [slot][quarter][lane] x 16 B: each wave instruction is 1 KiB contiguous
+                SA_LDS f32x4_t *dst = reinterpret_cast<SA_LDS f32x4_t *>(xo + (wave * C::TPR + t) * 4096) + lane;
 #pragma unroll
-        for (int k = 0; k < DH2; ++k) {  // own half: own a_s + partner's a_o, in place
-            const SA_LDS f32x4_t *src =
-                reinterpret_cast<const SA_LDS f32x4_t *>(xo + (((wave ^ 1) * DH2 + k) * 64 + lane) * 64);
-            f32x16_t &w = acc_o[R * DH2 + k];
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const f32x4_t x = src[q4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) w[4 * q4 + e] = fmaf(w[4 * q4 + e], a_s, x[e] * a_o);
+                for (int q4 = 0; q4 < 4; ++q4)
+                    dst[64 * q4] = f32x4_t{v[4 * q4], v[4 * q4 + 1], v[4 * q4 + 2], v[4 * q4 + 3]};
             }
-        }
-        if (split) {
-            // ---- split partials: unnormalised O, running max and sum, no sink ----
-            if (head_ok) {
-                const int64_t prow = ((int64_t)qi * p.n_sp + sp) * p.h + head;
-                float *po = p.part_o + prow * D + 4 * hf;
+            lds_barrier();
 #pragma unroll
-                for (int k = 0; k < DH2; ++k)
+            for (int t = 0; t < C::TPR; ++t) {  // own tiles: own a_s + partner's a_o
+                const int k = R * DH2 + r * C::TPR + t;  // d tile
+                const SA_LDS f32x4_t *src =
+                    reinterpret_cast<const SA_LDS f32x4_t *>(xo + ((wave ^ 1) * C::TPR + t) * 4096) + lane;
+                const f32x16_t &w = acc_o[k];
 #pragma unroll
-                    for (int qd = 0; qd < 4; ++qd) {
-                        const f32x16_t &o = acc_o[R * DH2 + k];
-                        *reinterpret_cast<f32x4_t *>(po + 32 * (R * DH2 + k) + 8 * qd) =
-                            f32x4_t{o[4 * qd], o[4 * qd + 1], o[4 * qd + 2], o[4 * qd + 3]};
+                for (int qd = 0; qd < 4; ++qd) {
+                    const f32x4_t x = src[64 * qd];
+                    const f32x4_t o = {fmaf(w[4 * qd], a_s, x[0] * a_o), fmaf(w[4 * qd + 1], a_s, x[1] * a_o),
+                                       fmaf(w[4 * qd + 2], a_s, x[2] * a_o), fmaf(w[4 * qd + 3], a_s, x[3] * a_o)};
+                    // lane (hf, n) holds head n, d = 32 k + 8 qd + 4 hf + (0..3)
+                    if (split) {
+                        if (head_ok)
+                            *reinterpret_cast<f32x4_t *>(p.part_o +
+                                                         (((int64_t)qi * p.n_sp + sp) * p.h + head) * D +
+                                                         32 * k + 8 * qd + 4 * hf) = o;
+                    } else {
+                        *reinterpret_cast<SA_LDS u32x2_t *>(stg + (hw * 32 + n) * C::RS + 64 * k + 16 * qd + 8 * hf) =
+                            u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
                     }
-                if (hf == 0 && R == 0) {
-                    p.part_ml[prow * 2] = M;
-                    p.part_ml[prow * 2 + 1] = Ls;
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            return;
         }
-        // ---- bf16 rows staged in LDS (over the merge area: after every wave's reads) ----
-        lds_barrier();
-        // lane (hf, n) holds head n, d = 32 dt + 8 qd + 4 hf + (0..3)
-        SA_LDS char *orow = (SA_LDS char *)smem + (hw * 32 + n) * C::RS + 8 * hf;
-#pragma unroll
-        for (int k = 0; k < DH2; ++k)
-#pragma unroll
-            for (int qd = 0; qd < 4; ++qd) {
-                const f32x16_t &o = acc_o[R * DH2 + k];
-                const u32x2_t w = {pack_bf16x2(o[4 * qd], o[4 * qd + 1]), pack_bf16x2(o[4 * qd + 2], o[4 * qd + 3])};
-                *reinterpret_cast<SA_LDS u32x2_t *>(orow + 64 * (R * DH2 + k) + 16 * qd) = w;
-            }
     };
     if (rh == 0)
         finish(std::integral_constant<int, 0>{});
     else
         finish(std::integral_constant<int, 1>{});
-    if (split) return;
+    if (split) {
+        if (head_ok && hf == 0 && rh == 0) {
+            const int64_t prow = ((int64_t)qi * p.n_sp + sp) * p.h + head;
+            p.part_ml[prow * 2] = M;
+            p.part_ml[prow * 2 + 1] = Ls;
+        }
+        return;
+    }
     lds_barrier();
     // one head row per wave instruction: lane l stores chunk l (16 B) of the row
 #pragma unroll 4
     for (int hr = wave; hr < C::HEADS; hr += C::NW) {
         const int hglob = (int)hg * C::HEADS + hr;
         if (hglob < p.h && chunk_lane) {
-            const u32x4_t v = *reinterpret_cast<const SA_LDS u32x4_t *>(lds + hr * C::RS + 16 * lane);
+            const u32x4_t v = *reinterpret_cast<const SA_LDS u32x4_t *>(stg + hr * C::RS + 16 * lane);
             *reinterpret_cast<u32x4_t *>(p.out + ((int64_t)qi * p.h + hglob) * D + lane * 8) = v;
         }
     }

@@ -122,6 +122,31 @@ def test_sparse_attn_small(case, variant):
     assert_parity(got, ref, f"case {case} variant {variant}")
 
 
+@pytest.mark.parametrize("d", [64, 512])
+@pytest.mark.parametrize("variant", [None, (1, 1), (1, 2), (2, 1)], ids=lambda v: "auto" if v is None else "k%d_sp%d" % v)
+def test_sparse_attn_scores_outrunning_the_first_stage(d, variant):
+    """The wide kernel takes the weights against the first max it sees and replays the
+    list when a later stage outruns it by more than 2^32.  Rows built from one query's
+    head row make that happen once (row 130, third 64-entry stage) and then again
+    (row 250, fourth stage, about 2^60 above the first replay's reference); the
+    result must still be the plain softmax."""
+    g = torch.Generator().manual_seed(77)
+    b, s, h, rows, topk = 2, 2, 64, 400, 320
+    q = torch.randn((b, s, h, d), generator=g).to(torch.bfloat16)
+    kv = (0.05 * torch.randn((b, rows, d), generator=g)).to(torch.bfloat16)
+    c1 = 60.0 / (d ** 0.5 * 1.4426950408889634)   # log2-domain score about 60 above the rest
+    for bi in range(b):
+        kv[bi, 130] = (c1 * q[bi, 0, 5].float()).to(torch.bfloat16)
+        kv[bi, 250] = (2.2 * c1 * q[bi, 0, 5].float()).to(torch.bfloat16)
+    idx = torch.arange(topk, dtype=torch.int32).repeat(b, s, 1).contiguous()
+    sink = torch.randn(h, generator=g)
+    got, ref = run_both(dict(q=q, kv=kv, sink=sink, idx=idx), variant)
+    assert_parity(got, ref, f"d {d} variant {variant}")
+    # the head the rows were built from is dominated by the last one
+    r = ref.reshape(b, s, h, d)[:, 0, 5]
+    assert np.allclose(r, kv[:, 250].float().numpy(), rtol=2e-2, atol=2e-2)
+
+
 def test_sparse_attn_edge_cases():
     # all -1, topk 0, sink -inf, invalid entries
     c = wl.small_case(21, 2, 3, 16, 512, 40, 40, 0.0)
