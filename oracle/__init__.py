@@ -58,10 +58,13 @@ def lib() -> ctypes.CDLL:
         L.sao_pow2_ceil.argtypes = [f32]
         L.sao_pow2_ceil.restype = f32
         L.sao_act_quant_fp8_inplace.argtypes = [vp, i64, i32]
+        L.sao_kv8_pack.argtypes = [vp, vp, vp, i64, i32]
+        L.sao_kv8_unpack.argtypes = [vp, vp, vp, i64, i32]
         L.sao_append_compressed_idxs.argtypes = [vp, i64, i32, vp, i64, i32, i32]
         L.sao_sparse_attn.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i64, i32, f32, vp, vp]
         for name in ("sao_window_topk_idxs_shape", "sao_window_topk_idxs", "sao_ring_write",
-                     "sao_act_quant_fp8_inplace", "sao_append_compressed_idxs", "sao_sparse_attn"):
+                     "sao_act_quant_fp8_inplace", "sao_append_compressed_idxs", "sao_sparse_attn",
+                     "sao_kv8_pack", "sao_kv8_unpack"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -125,6 +128,27 @@ def act_quant_fp8(x: np.ndarray) -> np.ndarray:
     y = np.ascontiguousarray(x).copy()
     act_quant_fp8_inplace(y)
     return y
+
+
+def kv8_pack(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """bf16 bits [..., row_len] -> (e4m3fn codes uint8 [..., row_len], E8M0 scale bytes [..., row_len // 32])."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    row_len = x.shape[-1]
+    n_rows = x.size // row_len if row_len else 0
+    codes = np.empty(x.shape, dtype=np.uint8)
+    scales = np.empty(x.shape[:-1] + (row_len // 32,), dtype=np.uint8)
+    _check("sao_kv8_pack", lib().sao_kv8_pack(_ptr(x), _ptr(codes), _ptr(scales), n_rows, row_len))
+    return codes, scales
+
+
+def kv8_unpack(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    row_len = codes.shape[-1]
+    n_rows = codes.size // row_len if row_len else 0
+    x = np.empty(codes.shape, dtype=np.uint16)
+    _check("sao_kv8_unpack", lib().sao_kv8_unpack(_ptr(codes), _ptr(scales), _ptr(x), n_rows, row_len))
+    return x
 
 
 def append_compressed_idxs(out: np.ndarray, col0: int, cidx: np.ndarray, offset: int) -> None:

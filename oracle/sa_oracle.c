@@ -211,6 +211,73 @@ int sao_act_quant_fp8_inplace(uint16_t *x, int64_t n_rows, int32_t row_len) {
     return SAO_OK;
 }
 
+/* ----------------------------------------- fp8-resident KV rows (kv8) --- */
+
+/* The fp8 round trip above keeps, per block of 32 values, an e4m3fn value times
+ * a power-of-two scale; a KV row can therefore be held as those e4m3fn codes
+ * (one byte per value) plus one scale byte per block, and expanded to exactly
+ * the bf16 values the round trip gives ([ATTN-RS] "Precision": bf16-exact).
+ * Scale bytes use the E8M0 encoding: byte b stands for 2^(b - 127). */
+
+/* OCP e4m3fn code of a value on the e4m3fn grid (|q| <= 448): sign bit, four
+ * exponent bits with bias 7, three mantissa bits; exponent field 0 holds the
+ * subnormals m * 2^-9 (and zero). */
+static uint8_t e4m3_code(float q) {
+    uint8_t sign = signbit(q) ? 0x80u : 0u;
+    float a = fabsf(q);
+    if (a < 0.015625f) return (uint8_t)(sign | (uint8_t)(a * 512.0f)); /* exact: a = m 2^-9 */
+    int e;
+    (void)frexpf(a, &e);                                   /* 2^(e-1) <= a < 2^e */
+    int ef = e - 1;                                         /* unbiased exponent */
+    int m = (int)((ldexpf(a, -ef) - 1.0f) * 8.0f);          /* exact: 3 mantissa bits */
+    return (uint8_t)(sign | (uint8_t)((ef + 7) << 3) | (uint8_t)m);
+}
+
+/* value of an e4m3fn code (0x7f and 0xff are NaN) */
+static float e4m3_value(uint8_t c) {
+    int ef = (c >> 3) & 15, m = c & 7;
+    if (ef == 15 && m == 7) return NAN;
+    float a = ef == 0 ? ldexpf((float)m, -9) : ldexpf(1.0f + (float)m / 8.0f, ef - 7);
+    return (c & 0x80u) ? -a : a;
+}
+
+/* bf16 rows [n_rows][row_len] -> codes [n_rows][row_len] and scale bytes
+ * [n_rows][row_len / 32], with the rounding of sao_act_quant_fp8_inplace. */
+int sao_kv8_pack(const uint16_t *x, uint8_t *codes, uint8_t *scales, int64_t n_rows, int32_t row_len) {
+    if (n_rows < 0 || row_len <= 0 || row_len % 32 != 0) return SAO_ERR_SHAPE;
+    if (n_rows == 0) return SAO_OK;
+    if (!x || !codes || !scales) return SAO_ERR_NULL;
+    int64_t nblocks = n_rows * (row_len / 32);
+#pragma omp parallel for schedule(static)
+    for (int64_t blk = 0; blk < nblocks; ++blk) {
+        const uint16_t *v = x + blk * 32;
+        float amax = 0.0f;
+        for (int i = 0; i < 32; ++i) {
+            float a = fabsf(bf16_to_f32(v[i]));
+            if (a > amax) amax = a;
+        }
+        if (amax < 1e-4f) amax = 1e-4f;
+        float scale = sao_pow2_ceil(amax / 448.0f);
+        int e;
+        (void)frexpf(scale, &e); /* scale = 2^(e-1) exactly */
+        scales[blk] = (uint8_t)(e - 1 + 127);
+        for (int i = 0; i < 32; ++i) codes[blk * 32 + i] = e4m3_code(e4m3_rne(bf16_to_f32(v[i]) / scale));
+    }
+    return SAO_OK;
+}
+
+/* codes + scale bytes -> bf16 rows: e4m3fn value times 2^(scale byte - 127) */
+int sao_kv8_unpack(const uint8_t *codes, const uint8_t *scales, uint16_t *x, int64_t n_rows, int32_t row_len) {
+    if (n_rows < 0 || row_len <= 0 || row_len % 32 != 0) return SAO_ERR_SHAPE;
+    if (n_rows == 0) return SAO_OK;
+    if (!x || !codes || !scales) return SAO_ERR_NULL;
+    int64_t n = n_rows * row_len;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        x[i] = f32_to_bf16(ldexpf(e4m3_value(codes[i]), (int)scales[i / 32] - 127));
+    return SAO_OK;
+}
+
 /* -------------------------------------- compressed-index concatenation --- */
 
 /* [QLAT] Attention.forward concatenates the window indices with the

@@ -313,6 +313,51 @@ def test_act_quant_invariants(oracle_lib):
     assert np.all(outv == 2.0 ** -30)  # 2^-30 / 2^-22 = 2^-8 = 2 * 2^-9, an e4m3 subnormal
 
 
+# ------------------------------------------- fp8-resident KV rows (kv8) --
+
+def test_kv8_code_values_match_the_e4m3fn_format(oracle_lib):
+    """Every one of the 256 codes, expanded at scale 2^0, against torch's
+    float8_e4m3fn reading of the same bit pattern (library routine)."""
+    codes = np.arange(256, dtype=np.uint8).reshape(8, 32)
+    scales = np.full((8, 1), 127, dtype=np.uint8)
+    got = oracle.kv8_unpack(codes, scales)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).float()
+    nan = torch.isnan(ref).numpy()
+    assert nan.sum() == 2 and nan.reshape(-1)[0x7f] and nan.reshape(-1)[0xff]
+    assert np.array_equal(got[~nan], bits(ref.to(torch.bfloat16))[~nan])
+
+
+def test_kv8_unpack_of_pack_is_the_fp8_round_trip(oracle_lib):
+    """Expanding the packed rows gives exactly the act_quant result, over every
+    finite bf16 value under many block scales (the exhaustive act_quant set)."""
+    from helpers import act_quant_blocks
+    blocks = act_quant_blocks()
+    codes, scales = oracle.kv8_pack(blocks)
+    assert np.array_equal(oracle.kv8_unpack(codes, scales), oracle.act_quant_fp8(blocks))
+
+
+def test_kv8_codes_and_scales_match_torch(oracle_lib):
+    """Codes are torch's float8_e4m3fn cast of x / scale; scale bytes are the
+    E8M0 exponent of pow2_ceil(max(amax, 1e-4) / 448)."""
+    g = torch.Generator().manual_seed(11)
+    x = (torch.randn((2048, 64), generator=g) * torch.exp(torch.randn((2048, 1), generator=g) * 4)).to(torch.bfloat16)
+    codes, scales = oracle.kv8_pack(bits(x))
+    xf = x.float().view(-1, 32)
+    amax = xf.abs().amax(dim=1, keepdim=True).clamp(min=1e-4)
+    ratio = amax / 448.0
+    scale = torch.exp2(torch.ceil(torch.log2(ratio)))
+    scale = torch.where(scale / 2 >= ratio, scale / 2, scale)
+    ref_codes = (xf / scale).to(torch.float8_e4m3fn).view(torch.uint8).view(x.shape).numpy()
+    ref_scales = (torch.log2(scale).round() + 127).to(torch.uint8).view(2048, 2).numpy()
+    assert np.array_equal(codes, ref_codes)
+    assert np.array_equal(scales, ref_scales)
+
+
+def test_kv8_shape_errors(oracle_lib):
+    with pytest.raises(oracle.OracleError):
+        oracle.kv8_pack(np.zeros((2, 33), dtype=np.uint16))
+
+
 def test_act_quant_shape_errors(oracle_lib):
     with pytest.raises(oracle.OracleError):
         oracle.act_quant_fp8(np.zeros((2, 48), dtype=np.uint16))
