@@ -104,6 +104,35 @@ sa_status sa_append_compressed_idxs(int32_t *idx, int64_t row_stride, int32_t co
 sa_status sa_act_quant_fp8_inplace(uint16_t *x, int64_t n_rows, int32_t row_len, void *stream);
 
 /* ------------------------------------------------------------------------
+ * fp8-resident KV rows ("kv8") -- [ATTN-RS] act_quant_inplace and "Precision":
+ * after the fp8 round trip each block of 32 values is an e4m3fn value times a
+ * power of two, so a row can be held as one e4m3fn byte per value plus one
+ * scale byte per block and expanded to exactly the same bf16 values.  Holding
+ * the cache this way halves the bytes (and, in the attention kernels, the copy
+ * instructions) of every gathered row; the attention results are identical.
+ *
+ *   codes  [n_rows][row_len]            uint8  OCP e4m3fn codes (sign, 4
+ *                                               exponent bits bias 7, 3
+ *                                               mantissa bits)
+ *   scales [n_rows][SA_KV8_SCALE_BYTES] uint8  E8M0 scale of block j (byte b:
+ *                                               scale 2^(b - 127)) in byte j <
+ *                                               row_len / 32; the remaining
+ *                                               bytes of the record are 127
+ *
+ * sa_kv8_pack: bf16 rows -> codes + scales, rounding as sa_act_quant_fp8_inplace
+ * (the input need not be rounded already).  sa_kv8_unpack: the inverse
+ * expansion, bit-identical to the fp8 round trip of the packed input.
+ * row_len a multiple of 32 (else SA_ERR_SHAPE) and at most 512
+ * (SA_ERR_UNSUPPORTED); every pointer 16-byte aligned (else SA_ERR_SHAPE). */
+#define SA_KV8_SCALE_BYTES 16
+
+sa_status sa_kv8_pack(const uint16_t *x, uint8_t *codes, uint8_t *scales, int64_t n_rows, int32_t row_len,
+                      void *stream);
+
+sa_status sa_kv8_unpack(const uint8_t *codes, const uint8_t *scales, uint16_t *x, int64_t n_rows,
+                        int32_t row_len, void *stream);
+
+/* ------------------------------------------------------------------------
  * Ring-cache update -- [ATTN-RS] ring-cache worked example (12 prefill tokens
  * into 8 slots leave slots 4..7 = tokens 4..7 and slots 0..3 = tokens 8..11;
  * decode step 12 writes slot 4, step 13 slot 5) and "the KV row rounded

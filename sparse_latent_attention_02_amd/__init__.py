@@ -12,6 +12,7 @@ Names follow the C ABI:
   window_kv_update                         -- fp8 round trip of new rows + ring-cache write
   sparse_attn                              -- the attention itself
   sparse_attn_decode_step                  -- a whole decode step (ring write, lists, attention) in one launch
+  kv8_pack / kv8_unpack                    -- fp8-resident KV rows (e4m3fn codes + E8M0 block scales)
 """
 from __future__ import annotations
 
@@ -26,6 +27,7 @@ _lib = None
 
 SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_UNSUPPORTED, SA_ERR_HIP = 0, 1, 2, 3, 4
 SA_KERNEL_AUTO, SA_KERNEL_WIDE, SA_KERNEL_DECODE = 0, 1, 2
+KV8_SCALE_BYTES = 16
 
 
 class SparseAttnError(RuntimeError):
@@ -58,13 +60,15 @@ def lib() -> ctypes.CDLL:
         L.sa_sparse_attn.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i64, i32, f32, vp, vp, sz, vp]
         L.sa_sparse_attn_ex.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i64, i32, f32, vp, vp, sz, vp,
                                         i32, i32]
+        L.sa_kv8_pack.argtypes = [vp, vp, vp, i64, i32, vp]
+        L.sa_kv8_unpack.argtypes = [vp, vp, vp, i64, i32, vp]
         L.sa_sparse_attn_decode_step_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, i32, i32]
         L.sa_sparse_attn_decode_step_workspace_bytes.restype = sz
         L.sa_sparse_attn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i64, i32, i32, i64, f32,
                                                  vp, vp, sz, vp, i32, i32]
         for fn in ("sa_window_topk_idxs_shape", "sa_window_topk_idxs", "sa_append_compressed_idxs",
                    "sa_act_quant_fp8_inplace", "sa_window_kv_update", "sa_sparse_attn", "sa_sparse_attn_ex",
-                   "sa_sparse_attn_decode_step"):
+                   "sa_sparse_attn_decode_step", "sa_kv8_pack", "sa_kv8_unpack"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -245,5 +249,40 @@ def sparse_attn_decode_step(q: torch.Tensor, kv: torch.Tensor, kv_new: torch.Ten
                                             idx_out.data_ptr() if idx_out is not None else None,
                                             b, h, d, rows, window, kc, start_pos, float(scale), out.data_ptr(),
                                             ws_ptr, ws_bytes, _stream(stream), k, sp))
+    return out
+
+
+def kv8_pack(x: torch.Tensor, codes: torch.Tensor | None = None, scales: torch.Tensor | None = None,
+             stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """bf16 rows [..., row_len] -> (uint8 codes [..., row_len], uint8 scales [..., 16])."""
+    _dev(x, "x", torch.bfloat16)
+    row_len = x.shape[-1]
+    n_rows = x.numel() // row_len if row_len else 0
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(x.shape[:-1] + (KV8_SCALE_BYTES,), dtype=torch.uint8, device=x.device)
+    _dev(codes, "codes", torch.uint8)
+    _dev(scales, "scales", torch.uint8)
+    if codes.numel() != x.numel() or scales.numel() != n_rows * KV8_SCALE_BYTES:
+        raise ValueError("codes must match x; scales must be [rows][16]")
+    _check("sa_kv8_pack", lib().sa_kv8_pack(x.data_ptr(), codes.data_ptr(), scales.data_ptr(), n_rows, row_len,
+                                            _stream(stream)))
+    return codes, scales
+
+
+def kv8_unpack(codes: torch.Tensor, scales: torch.Tensor, out: torch.Tensor | None = None,
+               stream=None) -> torch.Tensor:
+    _dev(codes, "codes", torch.uint8)
+    _dev(scales, "scales", torch.uint8)
+    row_len = codes.shape[-1]
+    n_rows = codes.numel() // row_len if row_len else 0
+    if scales.numel() != n_rows * KV8_SCALE_BYTES:
+        raise ValueError("scales must be [rows][16]")
+    if out is None:
+        out = torch.empty(codes.shape, dtype=torch.bfloat16, device=codes.device)
+    _dev(out, "out", torch.bfloat16)
+    _check("sa_kv8_unpack", lib().sa_kv8_unpack(codes.data_ptr(), scales.data_ptr(), out.data_ptr(), n_rows,
+                                                row_len, _stream(stream)))
     return out
 

@@ -43,10 +43,11 @@ __device__ __forceinline__ float e4m3_round(float y) {
     return __uint_as_float(__float_as_uint(r) | sign);
 }
 
-// fp8 round trip of one 16-byte chunk (8 bf16) whose 32-value block is spread
-// over lanes 4k..4k+3 of the wavefront; every lane of the wavefront must call
-// it (the block amax is reduced across the four lanes).
-__device__ __forceinline__ u32x4_t fp8_round_trip_chunk(u32x4_t w) {
+// Block rounding of one 16-byte chunk (8 bf16) whose 32-value block is spread
+// over lanes 4k..4k+3 of the wavefront; every lane of the wavefront must call it
+// (the block amax is reduced across the four lanes).  e[] receives the chunk's
+// values on the e4m3fn grid (before the scale), the return value is the scale.
+__device__ __forceinline__ float fp8_block_round(u32x4_t w, float e[8]) {
     float v[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -60,10 +61,61 @@ __device__ __forceinline__ u32x4_t fp8_round_trip_chunk(u32x4_t w) {
     amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
     amax = fmaxf(amax, 1e-4f);
     const float scale = pow2_ceil_ieee(amax / 448.0f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e[i] = e4m3_round(v[i] / scale);
+    return scale;
+}
+
+// fp8 round trip of one chunk: the rounded values times the scale, back in bf16
+// (exact: an e4m3fn value times a power of two)
+__device__ __forceinline__ u32x4_t fp8_round_trip_chunk(u32x4_t w) {
+    float e[8];
+    const float scale = fp8_block_round(w, e);
     u32x4_t o;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        o[i] = pack_bf16x2(e4m3_round(v[2 * i] / scale) * scale, e4m3_round(v[2 * i + 1] / scale) * scale);
+    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(e[2 * i] * scale, e[2 * i + 1] * scale);
+    return o;
+}
+
+// ---- fp8-resident KV rows: e4m3fn codes plus one E8M0 scale byte per block ----
+
+// OCP e4m3fn code of a value already on the e4m3fn grid (|q| <= 448), from its
+// f32 fields: sign, exponent rebiased from 127 to 7, the top 3 mantissa bits;
+// below 2^-6 the code is the subnormal count q / 2^-9 (exact).
+__device__ __forceinline__ uint32_t e4m3_code(float q) {
+    const uint32_t u = __float_as_uint(q);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7fffffffu;
+    if (a < 0x3c800000u) return sign | (uint32_t)(__uint_as_float(a) * 512.0f);
+    return sign | (((a >> 23) - 120u) << 3) | ((a >> 20) & 7u);
+}
+
+// Codes of one chunk (8 bytes, value i in byte i) and its block's scale byte
+// (the f32 biased exponent of the power-of-two scale, which is its E8M0 code).
+// Same lane contract as fp8_block_round.
+__device__ __forceinline__ u32x2_t fp8_pack_chunk(u32x4_t w, uint32_t &scale_byte) {
+    float e[8];
+    const float scale = fp8_block_round(w, e);
+    scale_byte = __float_as_uint(scale) >> 23;
+    u32x2_t c;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        c[j] = e4m3_code(e[4 * j]) | (e4m3_code(e[4 * j + 1]) << 8) | (e4m3_code(e[4 * j + 2]) << 16) |
+               (e4m3_code(e[4 * j + 3]) << 24);
+    return c;
+}
+
+// 8 codes of one block (byte i = value i) at scale 2^(scale_byte - 127) -> 8 bf16,
+// with the gfx950 scaled conversion (exact: each value is an e4m3fn value times a
+// power of two well inside the bf16 range).  scale_byte must lie in [1, 254].
+__device__ __forceinline__ u32x4_t kv8_expand(u32x2_t c, uint32_t scale_byte) {
+    const float sc = __uint_as_float(scale_byte << 23);
+    u32x4_t o;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        o[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[j], sc, false));
+        o[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[j], sc, true));
+    }
     return o;
 }
 

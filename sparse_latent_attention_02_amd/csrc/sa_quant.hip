@@ -53,6 +53,39 @@ __global__ void __launch_bounds__(256) window_kv_update_kernel(uint16_t *__restr
     *reinterpret_cast<u32x4_t *>(ring + ((bi * ring_stride + slot) * chunks_per_row + c) * 8) = o;
 }
 
+// fp8-resident KV rows: thread per 16-byte chunk (8 values); the 8 codes go to
+// codes[t * 8 ..], the first lane of each block writes its scale byte into the
+// row's 16-byte scale record (unused record bytes are set to 127, scale 2^0).
+__global__ void __launch_bounds__(256) kv8_pack_kernel(const uint16_t *__restrict__ x, uint8_t *__restrict__ codes,
+                                                       uint8_t *__restrict__ scales, int64_t n_chunks,
+                                                       int32_t chunks_per_row) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const bool live = t < n_chunks;
+    u32x4_t w = {0u, 0u, 0u, 0u};
+    if (live) w = *reinterpret_cast<const u32x4_t *>(x + t * 8);
+    uint32_t sb;
+    const u32x2_t c = fp8_pack_chunk(w, sb);
+    if (!live) return;
+    *reinterpret_cast<u32x2_t *>(codes + t * 8) = c;
+    const int64_t row = t / chunks_per_row;
+    const int32_t k = (int32_t)(t % chunks_per_row);
+    if ((k & 3) == 0) scales[row * SA_KV8_SCALE_BYTES + k / 4] = (uint8_t)sb;
+    if (k == 0)
+        for (int j = chunks_per_row / 4; j < SA_KV8_SCALE_BYTES; ++j) scales[row * SA_KV8_SCALE_BYTES + j] = 127;
+}
+
+__global__ void __launch_bounds__(256) kv8_unpack_kernel(const uint8_t *__restrict__ codes,
+                                                         const uint8_t *__restrict__ scales,
+                                                         uint16_t *__restrict__ x, int64_t n_chunks,
+                                                         int32_t chunks_per_row) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= n_chunks) return;
+    const int64_t row = t / chunks_per_row;
+    const int32_t k = (int32_t)(t % chunks_per_row);
+    const u32x2_t c = *reinterpret_cast<const u32x2_t *>(codes + t * 8);
+    *reinterpret_cast<u32x4_t *>(x + t * 8) = kv8_expand(c, scales[row * SA_KV8_SCALE_BYTES + k / 4]);
+}
+
 }  // namespace
 
 extern "C" sa_status sa_act_quant_fp8_inplace(uint16_t *x, int64_t n_rows, int32_t row_len,
@@ -85,5 +118,43 @@ extern "C" sa_status sa_window_kv_update(uint16_t *ring, int64_t ring_stride, ui
     if (blocks > 0x7fffffff) return SA_ERR_SHAPE;
     hipLaunchKernelGGL(window_kv_update_kernel, dim3((unsigned)blocks), dim3(threads), 0, (hipStream_t)stream,
                        ring, rows, n_chunks, d / 8, seqlen, window, ring_stride, start_pos);
+    return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+static sa_status kv8_args(int64_t n_rows, int32_t row_len) {
+    if (n_rows < 0 || row_len <= 0 || row_len % 32 != 0) return SA_ERR_SHAPE;
+    if (row_len > 32 * SA_KV8_SCALE_BYTES) return SA_ERR_UNSUPPORTED;
+    return SA_OK;
+}
+
+extern "C" sa_status sa_kv8_pack(const uint16_t *x, uint8_t *codes, uint8_t *scales, int64_t n_rows,
+                                 int32_t row_len, void *stream) {
+    sa_status st = kv8_args(n_rows, row_len);
+    if (st != SA_OK || n_rows == 0) return st;
+    if (!x || !codes || !scales) return SA_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(codes) | reinterpret_cast<uintptr_t>(scales)) %
+        16)
+        return SA_ERR_SHAPE;
+    const int64_t n_chunks = n_rows * (row_len / 8);
+    const int64_t blocks = (n_chunks + 255) / 256;
+    if (blocks > 0x7fffffff) return SA_ERR_SHAPE;
+    hipLaunchKernelGGL(kv8_pack_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, x, codes, scales,
+                       n_chunks, row_len / 8);
+    return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+extern "C" sa_status sa_kv8_unpack(const uint8_t *codes, const uint8_t *scales, uint16_t *x, int64_t n_rows,
+                                   int32_t row_len, void *stream) {
+    sa_status st = kv8_args(n_rows, row_len);
+    if (st != SA_OK || n_rows == 0) return st;
+    if (!x || !codes || !scales) return SA_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(codes) | reinterpret_cast<uintptr_t>(scales)) %
+        16)
+        return SA_ERR_SHAPE;
+    const int64_t n_chunks = n_rows * (row_len / 8);
+    const int64_t blocks = (n_chunks + 255) / 256;
+    if (blocks > 0x7fffffff) return SA_ERR_SHAPE;
+    hipLaunchKernelGGL(kv8_unpack_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, codes, scales,
+                       x, n_chunks, row_len / 8);
     return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
