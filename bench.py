@@ -7,6 +7,9 @@ lists built, compressed positions appended (when the workload has them) and
 the sparse attention itself -- all through the C ABI on one stream.  Decode
 workloads run the step as one launch (sa_sparse_attn_decode_step, the lists
 built inside the attention kernel); ``--unfused`` times the separate calls.
+``--kv8`` holds the decode cache fp8-resident (e4m3fn codes + E8M0 block
+scales) and runs the one-launch step on it: the same results, bit for bit,
+from about half the gathered bytes.
 
 Default workload: decode over the window ring, batch 64 single-query steps at
 position 5000, 64 heads, head dim 512, 128-slot ring (the configuration the
@@ -57,18 +60,23 @@ def parse():
     ap.add_argument("--unfused", action="store_true",
                     help="decode: run the step as separate calls (ring update, lists, attention) "
                          "instead of the one-launch decode step")
+    ap.add_argument("--kv8", action="store_true",
+                    help="decode: the cache held fp8-resident (e4m3fn codes + E8M0 block scales) and read "
+                         "and written in that form by the one-launch step (bitwise the same results)")
     ap.add_argument("--no-graphs", dest="graphs", action="store_false",
                     help="launch every step eagerly from Python instead of replaying HIP graphs")
     return ap.parse_args()
 
 
-def algorithmic_work(w, idx_sets, fused=False):
+def algorithmic_work(w, idx_sets, fused=False, kv8=False):
     """Algorithmic bytes and flops of one attention launch (valid entries only).
     Decode: every valid gathered row is HBM traffic (rows differ per sequence).
     Prefill: the unique KV rows referenced are read once; repeats come from cache.
     Fused decode step: the list is written instead of read (compressed entries
     still read), and the new row is read once and written once into the ring
-    (it enters the attention from registers instead of the ring)."""
+    (it enters the attention from registers instead of the ring).  kv8: a row is
+    d code bytes plus its 16-byte scale record; the new row is read as bf16 and
+    written as codes + record."""
     import torch
     idx = idx_sets[0]
     valid = int((idx >= 0).sum().item())
@@ -77,8 +85,9 @@ def algorithmic_work(w, idx_sets, fused=False):
     o_bytes = q_bytes
     idx_bytes = idx.numel() * 4
     sink_bytes = w.h * 4
+    row_bytes = w.d + 16 if kv8 else 2 * w.d
     if w.start_pos > 0:
-        kv_bytes = valid * w.d * 2
+        kv_bytes = valid * row_bytes
     else:
         uniq = 0
         for bi in range(w.b):
@@ -87,7 +96,7 @@ def algorithmic_work(w, idx_sets, fused=False):
         kv_bytes = uniq * w.d * 2
     if fused:
         idx_bytes += w.b * w.s * w.n_comp * 4
-        kv_bytes += w.b * w.d * 2
+        kv_bytes += w.b * w.d * 2     # new row: read raw + written, minus the gathered copy the count holds
     total = q_bytes + o_bytes + idx_bytes + sink_bytes + kv_bytes
     return dict(bytes=total, flops=flops, valid=valid, kv_bytes=kv_bytes)
 
@@ -100,10 +109,14 @@ def source_sha():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(wid, fused):
+def traffic_tag(wid, fused, kv8):
+    return f"w{wid}{'_kv8' if kv8 else ''}{'' if fused else '_unfused'}"
+
+
+def measured_traffic(tag):
     """HBM bytes per attention launch from the committed rocprofv3 counter summary,
     if it was taken on the current kernel source; else None."""
-    path = os.path.join(HERE, "profiles", f"attn_w{wid}{'' if fused else '_unfused'}_hbm_traffic.json")
+    path = os.path.join(HERE, "profiles", f"attn_{tag}_hbm_traffic.json")
     try:
         with open(path) as fh:
             t = json.load(fh)
@@ -224,16 +237,22 @@ def main():
 
     # ---- inputs resident in HBM, rotating sets for small workloads ----
     raw0 = wl.generate(args.workload)
-    sets = [pipeline.prepare(args.workload, raw0)]
-    pipeline.update_and_index(sets[0])
+    if args.kv8 and (w.start_pos == 0 or args.unfused):
+        print("bench.py: --kv8 applies to the one-launch decode step (workloads 2 and 4)", file=sys.stderr)
+        sys.exit(2)
+    sets = [pipeline.prepare(args.workload, raw0, kv8=args.kv8)]
+    pipeline.build_index(sets[0])
     torch.cuda.synchronize()
     fused = w.start_pos > 0 and not args.unfused
-    step_fn = pipeline.step_fused if fused else pipeline.step
-    kern_fn = pipeline.step_fused if fused else pipeline.attend    # the dominant kernel's launch
-    work = algorithmic_work(w, [sets[0].idx], fused)
+    if args.kv8:
+        step_fn = kern_fn = pipeline.step_fused_kv8
+    else:
+        step_fn = pipeline.step_fused if fused else pipeline.step
+        kern_fn = pipeline.step_fused if fused else pipeline.attend    # the dominant kernel's launch
+    work = algorithmic_work(w, [sets[0].idx], fused, args.kv8)
     n_sets = args.sets or max(1, min(48, math.ceil(2 * MALL_BYTES / work["bytes"])))
     for k in range(1, n_sets):
-        sets.append(pipeline.prepare(args.workload, wl.generate(args.workload, seed_offset=97 * k)))
+        sets.append(pipeline.prepare(args.workload, wl.generate(args.workload, seed_offset=97 * k), kv8=args.kv8))
     del raw0
     torch.cuda.synchronize()
 
@@ -323,7 +342,7 @@ def main():
         achieved = work["flops"] / (attn_mean / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
-    roof["traffic"] = measured_traffic(args.workload, fused or w.start_pos == 0)
+    roof["traffic"] = measured_traffic(traffic_tag(args.workload, fused or w.start_pos == 0, args.kv8))
     roof["algorithmic_bytes"] = work["bytes"]
     roof["algorithmic_flops"] = work["flops"]
     roof["kernel_ms_mean"] = round(attn_mean, 5)
@@ -346,6 +365,7 @@ def main():
                    "topk": w.topk, "kv_rows_per_seq": w.rows, "valid_entries": work["valid"],
                    "input_sets": n_sets, "launch": launch_desc,
                    "step": "one-launch decode step" if fused else "separate calls",
+                   "kv_cache": "fp8 e4m3fn codes + E8M0 block scales" if args.kv8 else "bf16",
                    "parallelism": "single GPU"},
         "roofline": roof,
         "wall_s": round(wall, 3),

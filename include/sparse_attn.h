@@ -199,12 +199,13 @@ sa_status sa_sparse_attn(const uint16_t *q, const uint16_t *kv, const float *sin
 /* Kernel variants of sa_sparse_attn_ex. */
 typedef enum {
     SA_KERNEL_AUTO = 0,
-    /* one workgroup per (query, 64 heads); each wavefront holds 32 heads
-     * (over half the head dim at d = 512); 32-row multi-buffered stages */
+    /* one workgroup of four wavefronts per (query, 64 heads); each wavefront
+     * holds 32 heads over the whole head dim and half of every 64-row stage;
+     * the list is compacted (-1 entries dropped) first; two stage buffers */
     SA_KERNEL_WIDE = 1,
-    /* one workgroup of four wavefronts per (query, 16 heads); 128-row stages
-     * whose rows the wavefronts split for the scores and whose head dim they
-     * split for the weighted sum (decode-sized batches) */
+    /* one workgroup of four wavefronts per (query, 16 heads); 64-row stages,
+     * two buffers deep, whose rows the wavefronts split for the scores and
+     * whose head dim they split for the weighted sum (decode-sized batches) */
     SA_KERNEL_DECODE = 2
 } sa_kernel;
 
@@ -271,6 +272,46 @@ sa_status sa_sparse_attn_decode_step(const uint16_t *q, uint16_t *kv, const uint
                                      int32_t kc, int64_t start_pos, float scale, uint16_t *out,
                                      void *workspace, size_t workspace_bytes, void *stream,
                                      int32_t kernel, int32_t splits);
+
+/* ------------------------------------------------------------------------
+ * Sparse latent attention over fp8-resident rows -- the operation of
+ * sa_sparse_attn and sa_sparse_attn_decode_step with the latent rows held as
+ * kv8 codes + scale records (layout as for sa_kv8_pack) instead of bf16:
+ *
+ *   kv_codes  [b][rows][d]                  uint8
+ *   kv_scales [b][rows][SA_KV8_SCALE_BYTES] uint8
+ *
+ * Each gathered row is expanded in LDS to exactly the bf16 values
+ * sa_kv8_unpack gives, so the output is bitwise that of sa_sparse_attn_ex
+ * (kernel SA_KERNEL_DECODE, same splits) on the unpacked rows.  The rows are
+ * read by the decode kernel only (it walks lists of any length; splits as for
+ * sa_sparse_attn_ex, 0 = automatic).  The decode step writes the new row's
+ * codes and scale record into ring slot start_pos % window of kv_codes /
+ * kv_scales: exactly what sa_kv8_pack stores for kv_new, whose expansion is
+ * the fp8 round trip of kv_new (the row the bf16 step writes).  (Packing that
+ * rounded row again can give other codes for the same values: a block whose
+ * amax rounds up onto 448 times a power of two gets half the scale.)  Nothing
+ * else of kv_codes / kv_scales is written.  Codes and scale records must come
+ * from sa_kv8_pack or an earlier decode step: a scale byte of 0 or 255 is a
+ * caller error (its rows expand to unspecified values, no out-of-bounds access
+ * results).  Every pointer of bf16 or kv8 data 16-byte aligned (else
+ * SA_ERR_SHAPE); the other rules are those of the bf16 entry points.
+ * workspace: sa_sparse_attn_kv8_workspace_bytes(b, s, h, d, topk, splits)
+ * bytes (for the decode step s = 1, topk = window + kc). */
+size_t sa_sparse_attn_kv8_workspace_bytes(int64_t b, int64_t s, int32_t h, int32_t d, int32_t topk,
+                                          int32_t splits);
+
+sa_status sa_sparse_attn_kv8(const uint16_t *q, const uint8_t *kv_codes, const uint8_t *kv_scales,
+                             const float *sink, const int32_t *idx, int64_t b, int64_t s, int32_t h,
+                             int32_t d, int64_t rows, int32_t topk, float scale, uint16_t *out,
+                             void *workspace, size_t workspace_bytes, void *stream, int32_t splits);
+
+sa_status sa_sparse_attn_decode_step_kv8(const uint16_t *q, uint8_t *kv_codes, uint8_t *kv_scales,
+                                         const uint16_t *kv_new, const float *sink, const int32_t *cidx,
+                                         int32_t *idx_out, int64_t b, int32_t h, int32_t d, int64_t rows,
+                                         int32_t window, int32_t kc, int64_t start_pos, float scale,
+                                         uint16_t *out, void *workspace, size_t workspace_bytes,
+                                         void *stream, int32_t splits);
 
 #ifdef __cplusplus
 }

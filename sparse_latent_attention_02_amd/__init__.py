@@ -13,6 +13,7 @@ Names follow the C ABI:
   sparse_attn                              -- the attention itself
   sparse_attn_decode_step                  -- a whole decode step (ring write, lists, attention) in one launch
   kv8_pack / kv8_unpack                    -- fp8-resident KV rows (e4m3fn codes + E8M0 block scales)
+  sparse_attn_kv8 / sparse_attn_decode_step_kv8 -- the attention and the decode step over kv8 rows
 """
 from __future__ import annotations
 
@@ -66,9 +67,16 @@ def lib() -> ctypes.CDLL:
         L.sa_sparse_attn_decode_step_workspace_bytes.restype = sz
         L.sa_sparse_attn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i64, i32, i32, i64, f32,
                                                  vp, vp, sz, vp, i32, i32]
+        L.sa_sparse_attn_kv8_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32]
+        L.sa_sparse_attn_kv8_workspace_bytes.restype = sz
+        L.sa_sparse_attn_kv8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i64, i32, f32, vp, vp, sz, vp,
+                                         i32]
+        L.sa_sparse_attn_decode_step_kv8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i64, i32, i32,
+                                                     i64, f32, vp, vp, sz, vp, i32]
         for fn in ("sa_window_topk_idxs_shape", "sa_window_topk_idxs", "sa_append_compressed_idxs",
                    "sa_act_quant_fp8_inplace", "sa_window_kv_update", "sa_sparse_attn", "sa_sparse_attn_ex",
-                   "sa_sparse_attn_decode_step", "sa_kv8_pack", "sa_kv8_unpack"):
+                   "sa_sparse_attn_decode_step", "sa_kv8_pack", "sa_kv8_unpack", "sa_sparse_attn_kv8",
+                   "sa_sparse_attn_decode_step_kv8"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -286,3 +294,93 @@ def kv8_unpack(codes: torch.Tensor, scales: torch.Tensor, out: torch.Tensor | No
                                                 row_len, _stream(stream)))
     return out
 
+
+
+def kv8_workspace_bytes(b: int, s: int, h: int, d: int, topk: int, splits: int = 0) -> int:
+    return int(lib().sa_sparse_attn_kv8_workspace_bytes(b, s, h, d, topk, splits))
+
+
+def _kv8_rows(codes: torch.Tensor, scales: torch.Tensor) -> tuple[int, int, int]:
+    _dev(codes, "kv_codes", torch.uint8)
+    _dev(scales, "kv_scales", torch.uint8)
+    if codes.dim() != 3 or scales.shape != codes.shape[:2] + (KV8_SCALE_BYTES,):
+        raise ValueError(f"kv_codes must be [b][rows][d] and kv_scales [b][rows][{KV8_SCALE_BYTES}], "
+                         f"got {tuple(codes.shape)} and {tuple(scales.shape)}")
+    return tuple(codes.shape)
+
+
+def _workspace(need: int, workspace: torch.Tensor | None, device) -> tuple:
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if workspace is None:
+        return None, 0
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def sparse_attn_kv8(q: torch.Tensor, kv_codes: torch.Tensor, kv_scales: torch.Tensor, sink: torch.Tensor,
+                    idx: torch.Tensor, scale: float, out: torch.Tensor | None = None,
+                    workspace: torch.Tensor | None = None, splits: int = 0, stream=None) -> torch.Tensor:
+    """sparse_attn over kv8 rows: kv_codes [b][rows][d] uint8, kv_scales [b][rows][16] uint8."""
+    _dev(q, "q", torch.bfloat16)
+    _dev(sink, "sink", torch.float32)
+    _dev(idx, "idx", torch.int32)
+    b, s, h, d = q.shape
+    kb, rows, kd = _kv8_rows(kv_codes, kv_scales)
+    if kb != b or kd != d:
+        raise ValueError(f"kv_codes must be [{b}][rows][{d}], got {tuple(kv_codes.shape)}")
+    if idx.dim() != 3 or idx.shape[0] != b or idx.shape[1] != s:
+        raise ValueError(f"idx must be [{b}][{s}][topk], got {tuple(idx.shape)}")
+    if sink.shape != (h,):
+        raise ValueError(f"sink must be [{h}]")
+    topk = idx.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", torch.bfloat16)
+    ws_ptr, ws_bytes = _workspace(kv8_workspace_bytes(b, s, h, d, topk, splits), workspace, q.device)
+    _check("sa_sparse_attn_kv8",
+           lib().sa_sparse_attn_kv8(q.data_ptr(), kv_codes.data_ptr(), kv_scales.data_ptr(), sink.data_ptr(),
+                                    idx.data_ptr(), b, s, h, d, rows, topk, float(scale), out.data_ptr(), ws_ptr,
+                                    ws_bytes, _stream(stream), splits))
+    return out
+
+
+def sparse_attn_decode_step_kv8(q: torch.Tensor, kv_codes: torch.Tensor, kv_scales: torch.Tensor,
+                                kv_new: torch.Tensor, sink: torch.Tensor, window: int, start_pos: int,
+                                scale: float, cidx: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                                idx_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                                splits: int = 0, stream=None) -> torch.Tensor:
+    """sparse_attn_decode_step over kv8 rows; the new row's codes and scale record
+    go to ring slot start_pos % window of kv_codes / kv_scales."""
+    _dev(q, "q", torch.bfloat16)
+    _dev(kv_new, "kv_new", torch.bfloat16)
+    _dev(sink, "sink", torch.float32)
+    b, rows, d = _kv8_rows(kv_codes, kv_scales)
+    h = q.shape[-2]
+    if q.numel() != b * h * d or q.shape[0] != b or q.shape[-1] != d:
+        raise ValueError(f"q must be [{b}][{h}][{d}] (or [{b}][1][{h}][{d}]), got {tuple(q.shape)}")
+    if kv_new.numel() != b * d or kv_new.shape[0] != b:
+        raise ValueError(f"kv_new must be [{b}][{d}], got {tuple(kv_new.shape)}")
+    if sink.shape != (h,):
+        raise ValueError(f"sink must be [{h}]")
+    kc = 0
+    if cidx is not None:
+        _dev(cidx, "cidx", torch.int32)
+        kc = cidx.shape[-1]
+        if cidx.numel() != b * kc:
+            raise ValueError(f"cidx must be [{b}][kc], got {tuple(cidx.shape)}")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", torch.bfloat16)
+    if idx_out is not None:
+        _dev(idx_out, "idx_out", torch.int32)
+        if idx_out.numel() != b * (window + kc):
+            raise ValueError(f"idx_out must hold [{b}][{window + kc}]")
+    ws_ptr, ws_bytes = _workspace(kv8_workspace_bytes(b, 1, h, d, window + kc, splits), workspace, q.device)
+    _check("sa_sparse_attn_decode_step_kv8",
+           lib().sa_sparse_attn_decode_step_kv8(q.data_ptr(), kv_codes.data_ptr(), kv_scales.data_ptr(),
+                                                kv_new.data_ptr(), sink.data_ptr(),
+                                                cidx.data_ptr() if cidx is not None else None,
+                                                idx_out.data_ptr() if idx_out is not None else None,
+                                                b, h, d, rows, window, kc, start_pos, float(scale),
+                                                out.data_ptr(), ws_ptr, ws_bytes, _stream(stream), splits))
+    return out

@@ -83,6 +83,13 @@ struct AttnParams {
     int32_t kc;              // compressed columns
     int32_t wbase;           // (pos + 1) % window: slot of the oldest entry
     int32_t new_slot;        // pos % window: slot of the new row (list entry window - 1)
+    // fp8-resident rows (kv8): e4m3fn codes [..][rows][d] and 16-byte scale
+    // records [..][rows][16] in place of kv; the fused step writes the new
+    // row's codes and scale record into its ring slot
+    const uint8_t *kv8c;
+    const uint8_t *kv8s;
+    uint8_t *kv8c_ring;
+    uint8_t *kv8s_ring;
 };
 
 // Entry e of a decode step's concatenated list: the ring listed oldest first,
@@ -612,13 +619,23 @@ struct DecodeCfg {
     static constexpr int PRS = 2 * ROWS + 16;     // padded row stride of the weight buffer P[head][row]
     static constexpr int STAGE_BYTES = ROWS * RS;
     static constexpr int Q_BYTES = HEADS * RS;
+    // kv8: a row's codes are D bytes, CPR8 16-byte chunks, RPI8 rows per copy
+    // instruction; a stage lands in an fp8 staging buffer (codes, then the rows'
+    // 16-byte scale records) and is expanded into the one bf16 stage buffer
+    static constexpr int CPR8 = D / 16;
+    static constexpr int RPI8 = 64 / CPR8;
+    static constexpr int NCI8 = RPW / RPI8;       // code copies per wave per stage (+1 for the scales)
+    static constexpr int STG8 = ROWS * D + ROWS * 16;
+    static constexpr int XPT = ROWS * (D / 8) / THREADS;  // bf16 chunks each thread expands per stage
     static_assert(KS >= 2 && KS % 2 == 0 && DT >= 1 && RPW == 16, "tiling");
+    static_assert(NCI8 >= 1 && (D / 8) <= 64 && XPT >= 1, "kv8 tiling");
 };
 
-template <int D, bool FUSED>
+template <int D, bool FUSED, bool KV8>
 __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
     using C = DecodeCfg<D>;
-    __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[(KV8 ? 1 : 2) * C::STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) char stg8[KV8 ? 2 * C::STG8 : 16];
     __shared__ __attribute__((aligned(16))) char qbuf[C::Q_BYTES];
     __shared__ __attribute__((aligned(16))) char pbuf[C::HEADS * C::PRS];
     __shared__ float smax[C::NW][16];
@@ -667,10 +684,28 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
     const int w_new = has_new ? (e_new % C::ROWS) / C::RPW : -1;
     const int u_new = has_new ? e_new % C::RPW : 0;
 
-    const uint16_t *kvb = p.kv + (int64_t)bi * p.rows * D;
+    const uint16_t *kvb = KV8 ? nullptr : p.kv + (int64_t)bi * p.rows * D;
+    const uint8_t *kcb = KV8 ? p.kv8c + (int64_t)bi * p.rows * D : nullptr;
+    const uint8_t *ksb = KV8 ? p.kv8s + (int64_t)bi * p.rows * 16 : nullptr;
     const uint32_t smem_base = lds_addr((const SA_LDS void *)smem);
+    const uint32_t stg8_base = lds_addr((const SA_LDS void *)stg8);
     const uint32_t q_base = lds_addr((const SA_LDS void *)qbuf);
     const SA_LDS char *lds = (const SA_LDS char *)smem;
+
+    // kv8 fused step: the new row never passes through the fp8 staging; the
+    // threads that expand its chunks (row r_new of stage st_new: expansion round
+    // k_new, wave w_conv, lanes from l_new) hold it raw from the start, round it
+    // through fp8 in registers and write both the bf16 values (into the stage) and
+    // the codes (into the ring, head group 0, at the end)
+    const int r_new = has_new ? w_new * C::RPW + u_new : 0;
+    const int k_new = (r_new * (D / 8)) / C::THREADS;
+    const int w_conv = ((r_new * (D / 8)) % C::THREADS) / 64;
+    const int l_new = (r_new * (D / 8)) % 64;
+    const bool holds_new = KV8 && has_new && wave == w_conv && lane >= l_new && lane < l_new + D / 8;
+    u32x4_t new_raw = {0u, 0u, 0u, 0u};
+    if (holds_new) new_raw = *reinterpret_cast<const u32x4_t *>(p.kv_new + (int64_t)qi * D + (lane - l_new) * 8);
+    u32x2_t new_codes = {0u, 0u};
+    uint32_t new_sb = 127;
 
     // fused step, head group 0: the list written out
     auto store_idx = [&](int j, int v) {
@@ -704,8 +739,44 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
         }
     };
 
+    // kv8 copies of stage j into staging buffer j % 2: instruction i < NCI8 carries
+    // RPI8 rows' codes (lane l: row i RPI8 + l / CPR8 of this wave, chunk l % CPR8),
+    // instruction NCI8 the 16 rows' scale records (lane u < 16: row u).  Lanes of an
+    // invalid row write zero codes (scale 2^0) instead; the fused step's new row is
+    // left to the threads that hold it.
+    auto copy8 = [&](int j, uint32_t okm, int rowv, int i0, int i1) {
+        const int sbuf = (j & 1) * C::STG8;
+        for (int i = i0; i < i1; ++i) {
+            if (i < C::NCI8) {
+                const int u = i * C::RPI8 + lane / C::CPR8;
+                const int row = __shfl(rowv, u, 64);
+                const bool live = ((okm >> u) & 1) && !(FUSED && has_new && j == st_new && wave == w_new && u == u_new);
+                const int off = sbuf + (wave * C::RPW + i * C::RPI8) * D;
+                if (live)
+                    dma_16B(kcb + (int64_t)row * D + 16 * (lane % C::CPR8),
+                            __builtin_amdgcn_readfirstlane(stg8_base + off));
+                else
+                    *reinterpret_cast<SA_LDS u32x4_t *>((SA_LDS char *)stg8 + off + 16 * lane) = u32x4_t{0u, 0u, 0u, 0u};
+            } else if (lane < 16) {
+                const bool live = ((okm >> lane) & 1) && !(FUSED && has_new && j == st_new && wave == w_new && lane == u_new);
+                const int off = sbuf + C::ROWS * D + wave * C::RPW * 16;
+                if (live)
+                    dma_16B(ksb + (int64_t)rowv * 16, __builtin_amdgcn_readfirstlane(stg8_base + off));
+                else
+                    *reinterpret_cast<SA_LDS u32x4_t *>((SA_LDS char *)stg8 + off + 16 * lane) =
+                        u32x4_t{0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu};
+            }
+        }
+    };
+    auto prep8 = [&](int v, uint32_t &okm, int &rowv) {
+        const bool ok = v >= 0 && (int64_t)v < p.rows;
+        okm = (uint32_t)__ballot(ok) & 0xffffu;
+        rowv = ok ? v : 0;
+    };
+
     uint32_t okm_cur = 0, okm_nxt = 0;
     uint64_t src_nxt = 0;
+    int rowv_nxt = 0;
     if (nst > 0) {
         store_idx(0, v0);
         // the query's head rows, once per workgroup: wavefront w copies heads 4w .. 4w+3
@@ -722,10 +793,17 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
                     u32x4_t{0u, 0u, 0u, 0u};
             }
         }
-        uint64_t src0;
-        prep(0, v0, okm_cur, src0);
+        if constexpr (KV8) {
+            int rowv0;
+            prep8(v0, okm_cur, rowv0);
 #pragma unroll 1
-        for (int u = 0; u < C::RPW; ++u) copy_rows(0, okm_cur, src0, u, u + 1);
+            for (int i = 0; i <= C::NCI8; ++i) copy8(0, okm_cur, rowv0, i, i + 1);
+        } else {
+            uint64_t src0;
+            prep(0, v0, okm_cur, src0);
+#pragma unroll 1
+            for (int u = 0; u < C::RPW; ++u) copy_rows(0, okm_cur, src0, u, u + 1);
+        }
     }
 
     const int head = (int)hg * C::HEADS + n;
@@ -741,10 +819,11 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
 
     for (int t = 0; t < nst; ++t) {
         const int ebase = lo + t * C::ROWS;
-        const SA_LDS char *stage = lds + (t & 1) * C::STAGE_BYTES;
+        const SA_LDS char *stage = lds + (KV8 ? 0 : (t & 1) * C::STAGE_BYTES);
         // ---- this wave's copies of stage t complete ----
         asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
-        if (FUSED && t == st_new && wave == w_new) {
+        if (KV8 && t == 0) asm volatile("" : : "v"(new_raw));  // (it was loaded before any copy)
+        if (!KV8 && FUSED && t == st_new && wave == w_new) {
             // the raw new row has landed: round it through fp8 in place
             SA_LDS u32x4_t *nr = reinterpret_cast<SA_LDS u32x4_t *>((SA_LDS char *)stage +
                                                                       (wave * C::RPW + u_new) * C::RS + 16 * lane);
@@ -753,10 +832,44 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
             if (chunk_lane) *nr = new_row;
         }
         lds_barrier();  // every wave's rows (and the head rows) in place; stage t-1 fully consumed
+        if constexpr (KV8) {
+            // ---- expand the stage's codes into the bf16 stage buffer ----
+            const SA_LDS char *s8 = (const SA_LDS char *)stg8 + (t & 1) * C::STG8;
+            u32x4_t nb = {0u, 0u, 0u, 0u};
+            if (FUSED && has_new && t == st_new && wave == w_conv) {  // wave-uniform: every lane rounds
+                float e[8];
+                const float sc = fp8_block_round(new_raw, e);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) nb[i] = pack_bf16x2(e[2 * i] * sc, e[2 * i + 1] * sc);
+                new_sb = __float_as_uint(sc) >> 23;
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+                    new_codes[jj] = e4m3_code(e[4 * jj]) | (e4m3_code(e[4 * jj + 1]) << 8) |
+                                    (e4m3_code(e[4 * jj + 2]) << 16) | (e4m3_code(e[4 * jj + 3]) << 24);
+            }
+#pragma unroll
+            for (int k = 0; k < C::XPT; ++k) {
+                const int gch = k * C::THREADS + tid;
+                const int r = gch / (D / 8), c = gch % (D / 8);
+                u32x4_t o;
+                if (FUSED && holds_new && t == st_new && k == k_new) {
+                    o = nb;
+                } else {
+                    const u32x2_t cd = *reinterpret_cast<const SA_LDS u32x2_t *>(s8 + r * D + 8 * c);
+                    const uint32_t sb = *reinterpret_cast<const SA_LDS uint8_t *>(s8 + C::ROWS * D + r * 16 + c / 4);
+                    o = kv8_expand(cd, sb);
+                }
+                *reinterpret_cast<SA_LDS u32x4_t *>((SA_LDS char *)smem + r * C::RS + 16 * c) = o;
+            }
+            lds_barrier();
+        }
         const bool more = t + 1 < nst;  // stage t+1 goes into the buffer stage t-1 used
         if (more) {
             store_idx(t + 1, v_up);
-            prep(t + 1, v_up, okm_nxt, src_nxt);
+            if constexpr (KV8)
+                prep8(v_up, okm_nxt, rowv_nxt);
+            else
+                prep(t + 1, v_up, okm_nxt, src_nxt);
         }
         if (t == 0) {
             // Q as the B operand of the scores: lane (g, n) holds q[head n][32 ks + 8 g .. +8]
@@ -772,7 +885,13 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
         for (int ks = 0; ks < C::KS; ks += 2) {
             const bf16x8_t a0 = lds_read_b128(kb + 64 * ks);
             const bf16x8_t a1 = lds_read_b128(kb + 64 * (ks + 1));
-            if (more) copy_rows(t + 1, okm_nxt, src_nxt, (ks / 2) * CPI, (ks / 2 + 1) * CPI);
+            if (more) {
+                if constexpr (KV8)
+                    copy8(t + 1, okm_nxt, rowv_nxt, (ks / 2) * (C::NCI8 + 1) / (C::KS / 2),
+                          (ks / 2 + 1) * (C::NCI8 + 1) / (C::KS / 2));
+                else
+                    copy_rows(t + 1, okm_nxt, src_nxt, (ks / 2) * CPI, (ks / 2 + 1) * CPI);
+            }
             s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qreg[ks], s0, 0, 0, 0);
             s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qreg[ks + 1], s1, 0, 0, 0);
         }
@@ -842,8 +961,18 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
     lds_barrier();
     const float l_tot = (ssum[0][n] + ssum[1][n]) + (ssum[2][n] + ssum[3][n]);
 
-    if (FUSED && hg == 0 && has_new && wave == w_new && chunk_lane)
+    if constexpr (KV8) {
+        if (FUSED && hg == 0 && holds_new) {
+            const int c = lane - l_new;
+            const int64_t rrow = (int64_t)bi * p.rows + p.new_slot;
+            *reinterpret_cast<u32x2_t *>(p.kv8c_ring + rrow * D + 8 * c) = new_codes;
+            if ((c & 3) == 0) p.kv8s_ring[rrow * 16 + c / 4] = (uint8_t)new_sb;
+            if (c == 0)
+                for (int j = D / 32; j < 16; ++j) p.kv8s_ring[rrow * 16 + j] = 127;
+        }
+    } else if (FUSED && hg == 0 && has_new && wave == w_new && chunk_lane) {
         *reinterpret_cast<u32x4_t *>(p.kv_ring + ((int64_t)bi * p.rows + p.new_slot) * D + lane * 8) = new_row;
+    }
 
     if (p.n_sp > 1) {
         if (head_ok) {
@@ -983,9 +1112,9 @@ hipError_t launch_wide(const AttnParams &p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int D, bool FUSED>
+template <int D, bool FUSED, bool KV8>
 hipError_t launch_decode(const AttnParams &p, hipStream_t stream) {
-    hipLaunchKernelGGL((sa_attn_decode<D, FUSED>), dim3((unsigned)p.total_wg), dim3(DecodeCfg<D>::THREADS), 0,
+    hipLaunchKernelGGL((sa_attn_decode<D, FUSED, KV8>), dim3((unsigned)p.total_wg), dim3(DecodeCfg<D>::THREADS), 0,
                        stream, p);
     return hipGetLastError();
 }
@@ -1000,16 +1129,17 @@ hipError_t launch_combine(const AttnParams &p, hipStream_t stream) {
 
 bool valid_d(int32_t d) { return d == 64 || d == 128 || d == 256 || d == 512; }
 
-template <bool FUSED>
+template <bool FUSED, bool KV8>
 hipError_t launch_attn(const AttnParams &p, const Variant &v, int32_t d, hipStream_t hs) {
     if (v.kernel == SA_KERNEL_DECODE) {
         switch (d) {
-            case 64: return launch_decode<64, FUSED>(p, hs);
-            case 128: return launch_decode<128, FUSED>(p, hs);
-            case 256: return launch_decode<256, FUSED>(p, hs);
-            default: return launch_decode<512, FUSED>(p, hs);
+            case 64: return launch_decode<64, FUSED, KV8>(p, hs);
+            case 128: return launch_decode<128, FUSED, KV8>(p, hs);
+            case 256: return launch_decode<256, FUSED, KV8>(p, hs);
+            default: return launch_decode<512, FUSED, KV8>(p, hs);
         }
     }
+    if (KV8) return hipErrorNotSupported;  // (resolve_variant keeps kv8 on the decode kernel)
     switch (d) {
         case 64: return launch_wide<64, FUSED>(p, hs);
         case 128: return launch_wide<128, FUSED>(p, hs);
@@ -1052,12 +1182,12 @@ AttnParams base_params(const uint16_t *q, const uint16_t *kv, const float *sink,
     return p;
 }
 
-template <bool FUSED>
+template <bool FUSED, bool KV8>
 sa_status enqueue(AttnParams &p, const Variant &v, int32_t d, hipStream_t hs) {
     const int64_t total = (int64_t)p.nq * p.n_hg * v.n_sp;
     if (total > 0x7fffffffLL) return SA_ERR_SHAPE;
     p.total_wg = (int32_t)total;
-    if (launch_attn<FUSED>(p, v, d, hs) != hipSuccess) return SA_ERR_HIP;
+    if (launch_attn<FUSED, KV8>(p, v, d, hs) != hipSuccess) return SA_ERR_HIP;
     if (v.n_sp > 1 && launch_combine_d(p, d, hs) != hipSuccess) return SA_ERR_HIP;
     return SA_OK;
 }
@@ -1070,7 +1200,27 @@ sa_status check_workspace(const Variant &v, int64_t nq, int32_t h, int32_t d, vo
     return SA_OK;
 }
 
-sa_status run_sparse_attn(const uint16_t *q, const uint16_t *kv, const float *sink, const int32_t *idx,
+// Where the latent rows live: bf16 rows, or fp8-resident codes + scale records.
+struct KvRows {
+    const uint16_t *kv = nullptr;
+    const uint8_t *kc = nullptr;
+    const uint8_t *ks = nullptr;
+    bool is8 = false;
+    bool kv8() const { return is8; }
+    bool present() const { return is8 ? (kc != nullptr && ks != nullptr) : kv != nullptr; }
+    uintptr_t bits() const {
+        return reinterpret_cast<uintptr_t>(kv) | reinterpret_cast<uintptr_t>(kc) | reinterpret_cast<uintptr_t>(ks);
+    }
+};
+
+// kv8 rows are read by the decode kernel only (it walks lists of any length)
+sa_status resolve_variant_kv(int64_t nq, int32_t h, int32_t topk, int32_t kernel, int32_t splits, bool kv8,
+                             Variant *out) {
+    if (kv8 && kernel == SA_KERNEL_WIDE) return SA_ERR_UNSUPPORTED;
+    return resolve_variant(nq, h, topk, kv8 ? SA_KERNEL_DECODE : kernel, splits, out);
+}
+
+sa_status run_sparse_attn(const uint16_t *q, const KvRows &kv, const float *sink, const int32_t *idx,
                           int64_t b, int64_t s, int32_t h, int32_t d, int64_t rows, int32_t topk,
                           float scale, uint16_t *out, void *workspace, size_t workspace_bytes,
                           void *stream, int32_t kernel, int32_t splits) {
@@ -1078,23 +1228,25 @@ sa_status run_sparse_attn(const uint16_t *q, const uint16_t *kv, const float *si
     if (!valid_d(d)) return SA_ERR_UNSUPPORTED;
     const int64_t nq = b * s;
     if (nq == 0 || h == 0) return SA_OK;
-    if (!q || !sink || !out || (topk > 0 && !idx) || (rows > 0 && !kv)) return SA_ERR_NULL;
+    if (!q || !sink || !out || (topk > 0 && !idx) || (rows > 0 && !kv.present())) return SA_ERR_NULL;
     if (rows > 0x7fffffffLL || nq > 0x7fffffffLL) return SA_ERR_SHAPE;
-    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(kv) | reinterpret_cast<uintptr_t>(out)) % 16)
-        return SA_ERR_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(q) | kv.bits() | reinterpret_cast<uintptr_t>(out)) % 16) return SA_ERR_SHAPE;
     Variant v;
-    sa_status st = resolve_variant(nq, h, topk, kernel, splits, &v);
+    sa_status st = resolve_variant_kv(nq, h, topk, kernel, splits, kv.kv8(), &v);
     if (st != SA_OK) return st;
     if ((st = check_workspace(v, nq, h, d, workspace, workspace_bytes)) != SA_OK) return st;
-    AttnParams p = base_params(q, kv, sink, nq, s, h, d, rows, topk, scale, out, workspace, v);
+    AttnParams p = base_params(q, kv.kv, sink, nq, s, h, d, rows, topk, scale, out, workspace, v);
+    p.kv8c = kv.kc;
+    p.kv8s = kv.ks;
     p.idx = idx;
-    return enqueue<false>(p, v, d, (hipStream_t)stream);
+    return kv.kv8() ? enqueue<false, true>(p, v, d, (hipStream_t)stream)
+                    : enqueue<false, false>(p, v, d, (hipStream_t)stream);
 }
 
 // Fused decode step: ring write of the new row (fp8 round trip), the window list,
 // the compressed append and the attention in one launch (plus the combine of a
 // split variant).
-sa_status run_decode_step(const uint16_t *q, uint16_t *kv, const uint16_t *kv_new, const float *sink,
+sa_status run_decode_step(const uint16_t *q, const KvRows &kv, const uint16_t *kv_new, const float *sink,
                           const int32_t *cidx, int32_t *idx_out, int64_t b, int32_t h, int32_t d, int64_t rows,
                           int32_t window, int32_t kc, int64_t start_pos, float scale, uint16_t *out,
                           void *workspace, size_t workspace_bytes, void *stream, int32_t kernel, int32_t splits) {
@@ -1104,18 +1256,22 @@ sa_status run_decode_step(const uint16_t *q, uint16_t *kv, const uint16_t *kv_ne
     if (rows < window || rows > 0x7fffffffLL || b > 0x7fffffffLL) return SA_ERR_SHAPE;
     if ((int64_t)window + kc > 0x7fffffffLL) return SA_ERR_SHAPE;
     if (b == 0 || h == 0) return SA_OK;
-    if (!q || !kv || !kv_new || !sink || !out || (kc > 0 && !cidx)) return SA_ERR_NULL;
-    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(kv) | reinterpret_cast<uintptr_t>(kv_new) |
+    if (!q || !kv.present() || !kv_new || !sink || !out || (kc > 0 && !cidx)) return SA_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(q) | kv.bits() | reinterpret_cast<uintptr_t>(kv_new) |
          reinterpret_cast<uintptr_t>(out)) % 16)
         return SA_ERR_SHAPE;
     const int32_t topk = window + kc;
     Variant v;
-    sa_status st = resolve_variant(b, h, topk, kernel, splits, &v);
+    sa_status st = resolve_variant_kv(b, h, topk, kernel, splits, kv.kv8(), &v);
     if (st != SA_OK) return st;
     if ((st = check_workspace(v, b, h, d, workspace, workspace_bytes)) != SA_OK) return st;
-    AttnParams p = base_params(q, kv, sink, b, 1, h, d, rows, topk, scale, out, workspace, v);
+    AttnParams p = base_params(q, kv.kv, sink, b, 1, h, d, rows, topk, scale, out, workspace, v);
     p.kv_new = kv_new;
-    p.kv_ring = kv;
+    p.kv_ring = const_cast<uint16_t *>(kv.kv);
+    p.kv8c = kv.kc;
+    p.kv8s = kv.ks;
+    p.kv8c_ring = const_cast<uint8_t *>(kv.kc);
+    p.kv8s_ring = const_cast<uint8_t *>(kv.ks);
     p.cidx = cidx;
     p.idx_out = idx_out;
     p.pos = start_pos;
@@ -1123,7 +1279,22 @@ sa_status run_decode_step(const uint16_t *q, uint16_t *kv, const uint16_t *kv_ne
     p.kc = kc;
     p.wbase = (int32_t)((start_pos + 1) % window);
     p.new_slot = (int32_t)(start_pos % window);
-    return enqueue<true>(p, v, d, (hipStream_t)stream);
+    return kv.kv8() ? enqueue<true, true>(p, v, d, (hipStream_t)stream)
+                    : enqueue<true, false>(p, v, d, (hipStream_t)stream);
+}
+
+KvRows bf16_rows(const uint16_t *kv) {
+    KvRows r;
+    r.kv = kv;
+    return r;
+}
+
+KvRows kv8_rows(const uint8_t *kc, const uint8_t *ks) {
+    KvRows r;
+    r.kc = kc;
+    r.ks = ks;
+    r.is8 = true;
+    return r;
 }
 
 }  // namespace
@@ -1147,16 +1318,16 @@ extern "C" sa_status sa_sparse_attn(const uint16_t *q, const uint16_t *kv, const
                                     const int32_t *idx, int64_t b, int64_t s, int32_t h, int32_t d,
                                     int64_t rows, int32_t topk, float scale, uint16_t *out, void *workspace,
                                     size_t workspace_bytes, void *stream) {
-    return run_sparse_attn(q, kv, sink, idx, b, s, h, d, rows, topk, scale, out, workspace, workspace_bytes,
-                           stream, 0, 0);
+    return run_sparse_attn(q, bf16_rows(kv), sink, idx, b, s, h, d, rows, topk, scale, out, workspace,
+                           workspace_bytes, stream, 0, 0);
 }
 
 extern "C" sa_status sa_sparse_attn_ex(const uint16_t *q, const uint16_t *kv, const float *sink,
                                        const int32_t *idx, int64_t b, int64_t s, int32_t h, int32_t d,
                                        int64_t rows, int32_t topk, float scale, uint16_t *out, void *workspace,
                                        size_t workspace_bytes, void *stream, int32_t kernel, int32_t splits) {
-    return run_sparse_attn(q, kv, sink, idx, b, s, h, d, rows, topk, scale, out, workspace, workspace_bytes,
-                           stream, kernel, splits);
+    return run_sparse_attn(q, bf16_rows(kv), sink, idx, b, s, h, d, rows, topk, scale, out, workspace,
+                           workspace_bytes, stream, kernel, splits);
 }
 
 extern "C" size_t sa_sparse_attn_decode_step_workspace_bytes(int64_t b, int32_t h, int32_t d, int32_t window,
@@ -1173,6 +1344,32 @@ extern "C" sa_status sa_sparse_attn_decode_step(const uint16_t *q, uint16_t *kv,
                                                 int32_t kc, int64_t start_pos, float scale, uint16_t *out,
                                                 void *workspace, size_t workspace_bytes, void *stream,
                                                 int32_t kernel, int32_t splits) {
-    return run_decode_step(q, kv, kv_new, sink, cidx, idx_out, b, h, d, rows, window, kc, start_pos, scale, out,
-                           workspace, workspace_bytes, stream, kernel, splits);
+    return run_decode_step(q, bf16_rows(kv), kv_new, sink, cidx, idx_out, b, h, d, rows, window, kc, start_pos,
+                           scale, out, workspace, workspace_bytes, stream, kernel, splits);
+}
+
+extern "C" size_t sa_sparse_attn_kv8_workspace_bytes(int64_t b, int64_t s, int32_t h, int32_t d, int32_t topk,
+                                                     int32_t splits) {
+    if (b < 0 || s < 0 || h <= 0 || topk < 0 || !valid_d(d)) return 0;
+    Variant v;
+    if (resolve_variant_kv(b * s, h, topk, 0, splits, true, &v) != SA_OK) return 0;
+    return workspace_for(v, b * s, h, d);
+}
+
+extern "C" sa_status sa_sparse_attn_kv8(const uint16_t *q, const uint8_t *kv_codes, const uint8_t *kv_scales,
+                                        const float *sink, const int32_t *idx, int64_t b, int64_t s, int32_t h,
+                                        int32_t d, int64_t rows, int32_t topk, float scale, uint16_t *out,
+                                        void *workspace, size_t workspace_bytes, void *stream, int32_t splits) {
+    return run_sparse_attn(q, kv8_rows(kv_codes, kv_scales), sink, idx, b, s, h, d, rows, topk, scale, out,
+                           workspace, workspace_bytes, stream, 0, splits);
+}
+
+extern "C" sa_status sa_sparse_attn_decode_step_kv8(const uint16_t *q, uint8_t *kv_codes, uint8_t *kv_scales,
+                                                    const uint16_t *kv_new, const float *sink, const int32_t *cidx,
+                                                    int32_t *idx_out, int64_t b, int32_t h, int32_t d, int64_t rows,
+                                                    int32_t window, int32_t kc, int64_t start_pos, float scale,
+                                                    uint16_t *out, void *workspace, size_t workspace_bytes,
+                                                    void *stream, int32_t splits) {
+    return run_decode_step(q, kv8_rows(kv_codes, kv_scales), kv_new, sink, cidx, idx_out, b, h, d, rows, window,
+                           kc, start_pos, scale, out, workspace, workspace_bytes, stream, 0, splits);
 }

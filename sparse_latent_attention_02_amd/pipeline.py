@@ -10,7 +10,10 @@ A step is what one layer does per forward call on its attention inputs:
   4. sparse attention over the selected rows (sa_sparse_attn).
 Everything runs through the C ABI on the current stream; torch only allocates.
 A decode step can also run as one launch (``step_fused``): the same four steps
-inside the attention kernel.
+inside the attention kernel.  With ``kv8`` the cache is held fp8-resident
+(e4m3fn codes + E8M0 block scales, sa_kv8_pack) and the one-launch step reads
+and writes it in that form (``step_fused_kv8``); the results are bitwise those
+of the bf16 cache.
 
 KV rows that exist before the step -- the ring contents at a decode step and
 the compressed cache -- are rounded through fp8 once in ``prepare``, as the cache
@@ -24,12 +27,15 @@ import torch
 
 from . import sparse_attn, window_kv_update, window_topk_idxs, append_compressed_idxs, act_quant_fp8_
 from . import workspace_bytes, sparse_attn_decode_step, decode_step_workspace_bytes
+from . import kv8_pack, kv8_workspace_bytes, sparse_attn_decode_step_kv8
 from .workloads import WORKLOADS
 
 
-def prepare(wid: int, raw: dict, device: str = "cuda") -> SimpleNamespace:
+def prepare(wid: int, raw: dict, device: str = "cuda", kv8: bool = False) -> SimpleNamespace:
     w = WORKLOADS[wid]
-    st = SimpleNamespace(w=w, wid=wid)
+    st = SimpleNamespace(w=w, wid=wid, kv8=kv8)
+    if kv8 and w.start_pos == 0:
+        raise ValueError("the fp8-resident cache is read by the decode step only")
     st.sink = raw["sink"].to(device)
     if wid == 1:
         st.q_prefill = raw["q_prefill"].to(device)
@@ -56,8 +62,20 @@ def prepare(wid: int, raw: dict, device: str = "cuda") -> SimpleNamespace:
     nws = workspace_bytes(w.b, w.s, w.h, w.d, w.topk)
     if w.start_pos > 0:
         nws = max(nws, decode_step_workspace_bytes(w.b, w.h, w.d, w.window, w.n_comp))
+    if kv8:
+        st.kc, st.ks = kv8_pack(st.kv)                     # the cache held as codes + scale records
+        st.kv = None
+        nws = max(nws, kv8_workspace_bytes(w.b, 1, w.h, w.d, w.topk))
     st.ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=device)
     return st
+
+
+def build_index(st: SimpleNamespace) -> None:
+    """Steps 2-3: the index list into ``st.idx``."""
+    w = st.w
+    window_topk_idxs(w.window, w.b, w.s, w.start_pos, out=st.idx)
+    if st.comp is not None:
+        append_compressed_idxs(st.idx, w.win_cols, st.comp, w.win_rows)
 
 
 def update_and_index(st: SimpleNamespace) -> None:
@@ -67,9 +85,7 @@ def update_and_index(st: SimpleNamespace) -> None:
         window_kv_update(st.kv, st.new_rows, w.start_pos, window=w.window)
     else:
         window_kv_update(st.ring, st.chunk, 0)
-    window_topk_idxs(w.window, w.b, w.s, w.start_pos, out=st.idx)
-    if st.comp is not None:
-        append_compressed_idxs(st.idx, w.win_cols, st.comp, w.win_rows)
+    build_index(st)
 
 
 def attend(st: SimpleNamespace) -> torch.Tensor:
@@ -113,3 +129,12 @@ def step_fused(st: SimpleNamespace) -> torch.Tensor:
                                    w.scale, cidx=st.comp.view(w.b, w.n_comp) if st.comp is not None else None,
                                    out=st.out, idx_out=st.idx, workspace=st.ws)
 
+
+def step_fused_kv8(st: SimpleNamespace) -> torch.Tensor:
+    """step_fused on the fp8-resident cache (sa_sparse_attn_decode_step_kv8): the
+    new row's codes and scale record go into its ring slot."""
+    w = st.w
+    return sparse_attn_decode_step_kv8(st.q, st.kc, st.ks, st.new_rows.view(w.b, w.d), st.sink, w.window,
+                                       w.start_pos, w.scale,
+                                       cidx=st.comp.view(w.b, w.n_comp) if st.comp is not None else None,
+                                       out=st.out, idx_out=st.idx, workspace=st.ws)

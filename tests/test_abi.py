@@ -77,3 +77,28 @@ def test_decode_step_argument_checks(lib):
     assert lib.sa_sparse_attn_decode_step_workspace_bytes(2, 4, 96, 8, 0, 0, 0) == 0
     assert lib.sa_sparse_attn_decode_step_workspace_bytes(64, 64, 512, 128, 0, 0, 0) == 0
     assert lib.sa_sparse_attn_decode_step_workspace_bytes(2, 64, 512, 128, 1024, 2, 4) == 2 * 4 * 64 * 514 * 4
+
+
+def test_kv8_attention_argument_checks(lib):
+    import sparse_latent_attention_02_amd as sa
+    f = lib.sa_sparse_attn_kv8
+    # (q, codes, scales, sink, idx, b, s, h, d, rows, topk, scale, out, ws, ws_bytes, stream, splits)
+    assert f(None, None, None, None, None, 1, 1, 4, 96, 8, 4, 0.1, None, None, 0, None, 0) == sa.SA_ERR_UNSUPPORTED
+    assert f(None, None, None, None, None, -1, 1, 4, 64, 8, 4, 0.1, None, None, 0, None, 0) == sa.SA_ERR_SHAPE
+    assert f(None, None, None, None, None, 0, 1, 4, 64, 8, 4, 0.1, None, None, 0, None, 0) == sa.SA_OK
+    assert f(None, None, None, None, None, 1, 1, 4, 64, 8, 4, 0.1, None, None, 0, None, 0) == sa.SA_ERR_NULL
+    assert f(None, None, None, None, None, 1, 1, 4, 64, 8, 4, 0.1, None, None, 0, None, -1) in \
+        (sa.SA_ERR_NULL, sa.SA_ERR_UNSUPPORTED)
+    g = lib.sa_sparse_attn_decode_step_kv8
+    # (q, codes, scales, kv_new, sink, cidx, idx_out, b, h, d, rows, window, kc, start_pos, scale, out, ws,
+    #  ws_bytes, stream, splits)
+    assert g(None, None, None, None, None, None, None, 2, 4, 64, 8, 8, 0, 0, 0.1, None, None, 0, None, 0) == \
+        sa.SA_ERR_UNSUPPORTED
+    assert g(None, None, None, None, None, None, None, 2, 4, 64, 7, 8, 0, 5, 0.1, None, None, 0, None, 0) == \
+        sa.SA_ERR_SHAPE
+    assert g(None, None, None, None, None, None, None, 2, 4, 64, 8, 8, 0, 5, 0.1, None, None, 0, None, 0) == \
+        sa.SA_ERR_NULL
+    # kv8 rows always go to the decode kernel: no workspace unless the list is split
+    assert lib.sa_sparse_attn_kv8_workspace_bytes(64, 1, 64, 512, 128, 0) == 0
+    assert lib.sa_sparse_attn_kv8_workspace_bytes(2, 1, 64, 512, 1152, 4) == 2 * 4 * 64 * 514 * 4
+    assert lib.sa_sparse_attn_kv8_workspace_bytes(2, 1, 64, 96, 1152, 4) == 0
