@@ -663,6 +663,11 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
 
     // this wave's 16 entries of a stage sit in lanes 0..15 (mirrored in the other
     // lane groups); the first three stages' go in flight before anything else
+    const int head = (int)hg * C::HEADS + n;
+    const bool head_ok = head < p.h;
+    // the head's sink, loaded before any copy goes out (a load issued after them
+    // would wait behind them at the end)
+    const float sink_h = head_ok ? p.sink[head] : 0.0f;
     const int eoff = C::RPW * wave + (lane & 15);
     auto fetch_stage = [&](int j) -> int {
         const int e = lo + j * C::ROWS + eoff;
@@ -806,8 +811,6 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
         }
     }
 
-    const int head = (int)hg * C::HEADS + n;
-    const bool head_ok = head < p.h;
     bf16x8_t qreg[C::KS];
     float m_ref = -1e30f;  // reference max (log2 domain), identical in all four wavefronts
     float l_run = 0.0f;    // this lane's share of the running sum over this wave's rows
@@ -941,14 +944,23 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
             if (32 * ks < hi - ebase) {  // k-steps past the list end hold only zero weights
                 const bf16x8_t pb =
                     lds_read_b128((const SA_LDS char *)pbuf + n * C::PRS + 2 * (32 * ks + 8 * g));
+                // all of the k-step's V reads go out ahead of its products
+                i16x4_t lo4[C::DT], hi4[C::DT];
 #pragma unroll
                 for (int dt = 0; dt < C::DT; ++dt) {
-                    const i16x4_t lo4 = lds_read_tr16(vb + (32 * ks) * C::RS + 32 * dt);
-                    const i16x4_t hi4 = lds_read_tr16(vb + (32 * ks + 4) * C::RS + 32 * dt);
-                    const bf16x8_t a =
-                        __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+                    lo4[dt] = lds_read_tr16(vb + (32 * ks) * C::RS + 32 * dt);
+                    hi4[dt] = lds_read_tr16(vb + (32 * ks + 4) * C::RS + 32 * dt);
+                }
+#pragma unroll
+                for (int dt = 0; dt < C::DT; ++dt) {
+                    const bf16x8_t a = __builtin_bit_cast(
+                        bf16x8_t, __builtin_shufflevector(lo4[dt], hi4[dt], 0, 1, 2, 3, 4, 5, 6, 7));
                     acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, acc_o[dt], 0, 0, 0);
                 }
+#pragma unroll
+                for (int i = 0; i < 2 * C::DT + 1; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+                for (int i = 0; i < C::DT; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             }
         }
         okm_cur = okm_nxt;
@@ -987,15 +999,26 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
         }
         return;
     }
-    if (!head_ok) return;
-    const float Lt = l_tot + exp2_fast(p.sink[head] * kLog2e - m_ref);
+    const float Lt = l_tot + exp2_fast(sink_h * kLog2e - m_ref);
     const float inv = Lt > 0.f ? 1.0f / Lt : 0.f;
-    // lane (g, n) holds head n, d = quarter + 16 dt + 4 g + (0..3)
-    uint16_t *orow = p.out + ((int64_t)qi * p.h + head) * D + C::DQ * wave + 4 * g;
+    // lane (g, n) holds head n, d = quarter + 16 dt + 4 g + (0..3); the rows are
+    // assembled in the head-row buffer (read into registers at the first stage)
+    // so that every output store below writes a whole row
+    SA_LDS char *orow = (SA_LDS char *)qbuf + n * C::RS + 2 * (C::DQ * wave + 4 * g);
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
         const f32x4_t o = acc_o[dt] * inv;
-        *reinterpret_cast<u32x2_t *>(orow + 16 * dt) = u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        *reinterpret_cast<SA_LDS u32x2_t *>(orow + 32 * dt) = u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    }
+    lds_barrier();
+    // one head row per wave instruction: lane l stores 16-byte chunk l of the row
+#pragma unroll
+    for (int r = 0; r < C::HEADS / C::NW; ++r) {
+        const int hr = wave + C::NW * r;
+        const int hglob = (int)hg * C::HEADS + hr;
+        if (hglob < p.h && chunk_lane)
+            *reinterpret_cast<u32x4_t *>(p.out + ((int64_t)qi * p.h + hglob) * D + lane * 8) =
+                *reinterpret_cast<const SA_LDS u32x4_t *>((const SA_LDS char *)qbuf + hr * C::RS + 16 * lane);
     }
 }
 
