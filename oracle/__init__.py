@@ -9,8 +9,9 @@ never do.  Every array is a numpy array on the host; bf16 tensors travel as
 Each function follows the page passage cited in ``sa_oracle.c``:
 window selection and the sparse_attn kernel from "DeepSeek V4.1 ... attention /
 attend"; the index concatenation from "... attention / query-latent"
-(Attention.forward, Indexer tail); the ring write, fp8 round trip and
-pow2_ceil from the "Module attn" rustdoc page.
+(Attention.forward, Indexer tail) and the rotary embedding (apply_rotary_emb);
+the ring write, fp8 round trip, pow2_ceil and apply_rotary contract from the
+"Module attn" rustdoc page.
 """
 from __future__ import annotations
 
@@ -62,9 +63,10 @@ def lib() -> ctypes.CDLL:
         L.sao_kv8_unpack.argtypes = [vp, vp, vp, i64, i32]
         L.sao_append_compressed_idxs.argtypes = [vp, i64, i32, vp, i64, i32, i32]
         L.sao_sparse_attn.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i64, i32, f32, vp, vp]
+        L.sao_apply_rotary.argtypes = [vp, i64, i64, i32, i32, i32, vp, i64, i64, ctypes.c_int]
         for name in ("sao_window_topk_idxs_shape", "sao_window_topk_idxs", "sao_ring_write",
                      "sao_act_quant_fp8_inplace", "sao_append_compressed_idxs", "sao_sparse_attn",
-                     "sao_kv8_pack", "sao_kv8_unpack"):
+                     "sao_kv8_pack", "sao_kv8_unpack", "sao_apply_rotary"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -183,3 +185,17 @@ def sparse_attn(q: np.ndarray, kv: np.ndarray, sink: np.ndarray, idx: np.ndarray
            lib().sao_sparse_attn(_ptr(q), _ptr(kv), _ptr(sink), _ptr(idx), b, s, h, d, rows, topk,
                                  float(scale), _ptr(out), _ptr(out32)))
     return (out, out32) if want_f32 else out
+
+
+def apply_rotary(x: np.ndarray, table: np.ndarray, rope_dim: int, start_pos: int, inverse: bool) -> np.ndarray:
+    """Rotary embedding of the last ``rope_dim`` values of bf16 bits ``x``
+    [b][s][h][row_len] (or [b][s][row_len]); row (b, s, .) at position start_pos + s.
+    ``table`` [n_pos][rope_dim / 2][2] f32 (cos, sin).  Returns a rotated copy."""
+    y = np.ascontiguousarray(x, dtype=np.uint16).copy()
+    shp = y.shape
+    b, s = shp[0], shp[1]
+    h = shp[2] if y.ndim == 4 else 1
+    t = np.ascontiguousarray(table, dtype=np.float32)
+    _check("sao_apply_rotary", lib().sao_apply_rotary(_ptr(y), b, s, h, shp[-1], rope_dim, _ptr(t), t.shape[0],
+                                                       start_pos, int(bool(inverse))))
+    return y

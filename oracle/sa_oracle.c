@@ -14,7 +14,9 @@
  *             (window/compressed concatenation), Indexer tail (offset, -1).
  *   [ATTN-RS] "Module attn" (deepseek_v41_ref attn rustdoc): precision
  *             contract, ring-cache worked example, act_quant_inplace,
- *             pow2_ceil, sparse_attn, window_topk_idxs contracts.
+ *             pow2_ceil, sparse_attn, window_topk_idxs, apply_rotary contracts.
+ *   [ROPE]    "DeepSeek V4.1 ... attention / query-latent": apply_rotary_emb
+ *             and its use on the attention output (inverse rotation).
  *
  * Arithmetic: sparse_attn in f32 as [ATTN-RS] "Precision" fixes it (f32
  * softmax, bf16 result).  It is written as the plain two-pass softmax
@@ -382,4 +384,52 @@ int sao_sparse_attn(const uint16_t *q, const uint16_t *kv, const float *sink,
         }
     }
     return bad ? SAO_ERR_UNSUPPORTED : SAO_OK;
+}
+
+/* ------------------------------------------------------ rotary embedding --- */
+
+/* [ATTN-RS] apply_rotary, [ROPE] apply_rotary_emb: rotate the last rope_dim
+ * values of every row_len-wide row of x [b][s][h][row_len] in place; row
+ * (bi, si, hi) sits at position start_pos + si.  Adjacent pairs (x[2j],
+ * x[2j+1]) of the rotated part are the complex number a + i b, multiplied in
+ * f32 by the table entry (c, sn) of that position and pair -- by its conjugate
+ * c - i sn when inverse (the output's un-rotation after sparse_attn) -- and
+ * written back as bf16 (round to nearest even).  The f32 complex product rounds
+ * each real product, then the sum:
+ *   forward: re = a c - b sn,   im = a sn + b c
+ *   inverse: re = a c + b sn,   im = b c - a sn
+ *   table [n_pos][rope_dim / 2][2] f32 (cos, sin) of position p, pair j.
+ * rope_dim must be even and at most row_len (else SAO_ERR_SHAPE); every
+ * position start_pos + si must lie in [0, n_pos) (else SAO_ERR_INDEX). */
+int sao_apply_rotary(uint16_t *x, int64_t b, int64_t s, int32_t h, int32_t row_len, int32_t rope_dim,
+                     const float *table, int64_t n_pos, int64_t start_pos, int inverse) {
+    if (b < 0 || s < 0 || h < 0 || row_len < 0 || rope_dim < 0 || n_pos < 0) return SAO_ERR_SHAPE;
+    if (rope_dim % 2 != 0 || rope_dim > row_len) return SAO_ERR_SHAPE;
+    if (b * s * h == 0 || rope_dim == 0) return SAO_OK;
+    if (!x || !table) return SAO_ERR_NULL;
+    if (start_pos < 0 || start_pos + s > n_pos) return SAO_ERR_INDEX;
+    const int32_t half = rope_dim / 2;
+    for (int64_t bi = 0; bi < b; ++bi)
+        for (int64_t si = 0; si < s; ++si) {
+            const float *tp = table + (start_pos + si) * (int64_t)half * 2;
+            for (int32_t hi = 0; hi < h; ++hi) {
+                uint16_t *row = x + ((bi * s + si) * h + hi) * (int64_t)row_len + (row_len - rope_dim);
+                for (int32_t j = 0; j < half; ++j) {
+                    const float a = bf16_to_f32(row[2 * j]), bb = bf16_to_f32(row[2 * j + 1]);
+                    const float c = tp[2 * j], sn = tp[2 * j + 1];
+                    const float ac = a * c, bs = bb * sn, as = a * sn, bc = bb * c;
+                    float re, im;
+                    if (inverse) {
+                        re = ac + bs;
+                        im = bc - as;
+                    } else {
+                        re = ac - bs;
+                        im = as + bc;
+                    }
+                    row[2 * j] = f32_to_bf16(re);
+                    row[2 * j + 1] = f32_to_bf16(im);
+                }
+            }
+        }
+    return SAO_OK;
 }

@@ -526,3 +526,82 @@ def test_workload_generators_shapes():
     b = wl.generate(1)
     assert torch.equal(a["q_prefill"], b["q_prefill"]) and torch.equal(a["sink"], b["sink"])
     assert a["kv_prefill"].shape == (1, 12, 64) and a["q_dec"].shape == (2, 1, 1, 4, 64)
+
+
+# ------------------------------------------------------ rotary embedding --
+
+def _bf16_round(x: np.ndarray) -> np.ndarray:
+    return bits(torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16))
+
+
+def _angles_table(g, n_pos, half):
+    th = (torch.rand((n_pos, half), generator=g, dtype=torch.float64) * 2 - 1) * math.pi
+    return np.stack([np.cos(th.numpy()), np.sin(th.numpy())], axis=-1).astype(np.float32), th.numpy()
+
+
+def test_rotary_identity_and_quarter_turns(oracle_lib):
+    """cos/sin tables of 0, pi/2, pi: the products are exact, so the rotation is a
+    permutation / sign change of the pair, and the first row_len - rope_dim values
+    are never touched."""
+    g = torch.Generator().manual_seed(71)
+    x = bits(torch.randn((2, 3, 4, 128), generator=g).to(torch.bfloat16))
+    rd, half = 64, 32
+    f = bf16_to_f64(x)
+    for cs, fwd in (((1.0, 0.0), lambda a, b: (a, b)), ((0.0, 1.0), lambda a, b: (-b, a)),
+                    ((-1.0, 0.0), lambda a, b: (-a, -b))):
+        table = np.tile(np.array(cs, dtype=np.float32), (3, half, 1))
+        for inverse in (False, True):
+            y = oracle.apply_rotary(x, table, rd, 0, inverse)
+            assert np.array_equal(y[..., :128 - rd], x[..., :128 - rd])
+            a, b = f[..., 128 - rd::2], f[..., 128 - rd + 1::2]
+            ea, eb = fwd(a, b) if not inverse else fwd(a, -b)
+            if inverse:
+                eb = -eb                       # conj(z) rotated back: (a, b) * conj(c + i s)
+            got = bf16_to_f64(y)
+            assert np.array_equal(got[..., 128 - rd::2], ea), (cs, inverse)
+            assert np.array_equal(got[..., 128 - rd + 1::2], eb), (cs, inverse)
+
+
+@pytest.mark.parametrize("inverse", [False, True])
+def test_rotary_matches_complex128_product(oracle_lib, inverse):
+    """Against numpy's complex128 product of the same bf16 pairs by the same f32
+    table (conjugated for the inverse): the f32 arithmetic stays within its
+    rounding bound, and the bf16 result within one bf16 ulp of the exact product
+    rounded."""
+    g = torch.Generator().manual_seed(72 + inverse)
+    b, s, h, d, rd, pos0 = 2, 5, 3, 192, 64, 7
+    x = bits((torch.randn((b, s, h, d), generator=g) * torch.exp(torch.randn((b, s, h, 1), generator=g))).to(
+        torch.bfloat16))
+    table, _ = _angles_table(g, pos0 + s, rd // 2)
+    y = oracle.apply_rotary(x, table, rd, pos0, inverse)
+    f = bf16_to_f64(x)
+    z = f[..., d - rd::2] + 1j * f[..., d - rd + 1::2]
+    w = table[pos0:pos0 + s, :, 0].astype(np.float64) + 1j * table[pos0:pos0 + s, :, 1].astype(np.float64)
+    w = w[None, :, None, :]
+    ex = z * (np.conj(w) if inverse else w)
+    got = bf16_to_f64(y)
+    for part, e in ((got[..., d - rd::2], ex.real), (got[..., d - rd + 1::2], ex.imag)):
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(e), 1e-30))) - 7)
+        bound = ulp + 2.0 ** -22 * (np.abs(z.real) + np.abs(z.imag))
+        assert np.all(np.abs(part - e) <= bound)
+        assert np.mean(part == bf16_to_f64(_bf16_round(e))) > 0.97
+    assert np.array_equal(y[..., :d - rd], x[..., :d - rd])
+
+
+def test_rotary_inverse_undoes_forward(oracle_lib):
+    g = torch.Generator().manual_seed(74)
+    x = bits(torch.randn((1, 9, 2, 64), generator=g).to(torch.bfloat16))
+    table, _ = _angles_table(g, 20, 32)
+    back = oracle.apply_rotary(oracle.apply_rotary(x, table, 64, 11, False), table, 64, 11, True)
+    f, r = bf16_to_f64(x), bf16_to_f64(back)
+    mag = np.repeat(np.hypot(f[..., 0::2], f[..., 1::2]), 2, axis=-1)
+    assert np.all(np.abs(r - f) <= 2.0 ** -7 * mag + 1e-30)
+
+
+def test_rotary_shape_errors(oracle_lib):
+    x = np.zeros((1, 2, 1, 64), dtype=np.uint16)
+    t = np.zeros((4, 16, 2), dtype=np.float32)
+    for rd, pos, st in ((31, 0, oracle.ERR_SHAPE), (66, 0, oracle.ERR_SHAPE), (32, 3, oracle.ERR_INDEX)):
+        with pytest.raises(oracle.OracleError) as e:
+            oracle.apply_rotary(x, t, rd, pos, True)
+        assert e.value.status == st
