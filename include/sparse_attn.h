@@ -10,7 +10,10 @@
  *             (concatenation of window and compressed indices), Indexer tail.
  *   [ATTN-RS] "Module attn" rustdoc (DeepSeek-V4.1 reference, ratio-0
  *             attention) -- precision contract, ring-cache worked example,
- *             act_quant_inplace, pow2_ceil, sparse_attn, window_topk_idxs.
+ *             act_quant_inplace, pow2_ceil, sparse_attn, window_topk_idxs,
+ *             apply_rotary.
+ *   [ROPE]    "DeepSeek V4.1 ... attention / query-latent" -- apply_rotary_emb
+ *             and the inverse rotation of the attention output.
  *
  * Conventions for every entry point:
  *   - bf16 tensors are passed as uint16_t bit patterns; f32 as float.
@@ -312,6 +315,53 @@ sa_status sa_sparse_attn_decode_step_kv8(const uint16_t *q, uint8_t *kv_codes, u
                                          int32_t window, int32_t kc, int64_t start_pos, float scale,
                                          uint16_t *out, void *workspace, size_t workspace_bytes,
                                          void *stream, int32_t splits);
+
+/* ------------------------------------------------------------------------
+ * Rotary embedding -- [ATTN-RS] apply_rotary, [ROPE] apply_rotary_emb.
+ *
+ *   x     [b][s][h][row_len] bf16, modified in place (h = 1 for [b][s][row_len])
+ *   table [n_pos][rope_dim / 2][2] f32: (cos, sin) of position p, pair j
+ * The last rope_dim values of every row are rotated; row (bi, si, hi) sits at
+ * position start_pos + si.  Pair j of the rotated part, (a, b) = (x[2j],
+ * x[2j+1]), is the complex number a + i b, multiplied in f32 by cos + i sin
+ * (inverse != 0: by cos - i sin, which removes a rotation) -- each real product
+ * rounded, then the sum, no fused multiply-add -- and stored as bf16 (round to
+ * nearest even):
+ *   forward: (a cos - b sin, a sin + b cos)   inverse: (a cos + b sin, b cos - a sin)
+ * Bit-exact against that definition.  rope_dim even and <= row_len, row_len
+ * even, start_pos + s <= n_pos (else SA_ERR_SHAPE); x 4-byte and table 8-byte
+ * aligned (else SA_ERR_SHAPE). */
+sa_status sa_apply_rotary(uint16_t *x, int64_t b, int64_t s, int32_t h, int32_t row_len, int32_t rope_dim,
+                          const float *table, int64_t n_pos, int64_t start_pos, int32_t inverse, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Sparse latent attention with the output's inverse rotation fused into its
+ * epilogue -- [ROPE] Attention.forward: after sparse_attn the last rope_dim
+ * values of the output are un-rotated at the query's position
+ * (apply_rotary_emb(o[..., -rd:], freqs_cis, inverse=True)).
+ *
+ * Same result, bit for bit, as the unfused pair of calls
+ *   sa_sparse_attn_ex(..., kernel, splits)   (resp. sa_sparse_attn_decode_step)
+ *   sa_apply_rotary(out, b, s, h, d, rope_dim, rope_table, n_pos, start_pos, 1)
+ * (the rounded bf16 output is rotated, as the pages round before rotating),
+ * without the second pass over the output.  Query si of a sequence sits at
+ * position start_pos + si (the decode step: start_pos).  rope_table as for
+ * sa_apply_rotary, 16-byte aligned; rope_dim a multiple of 8 in [8, d];
+ * positions within [0, n_pos) (else SA_ERR_SHAPE); NULL rope_table:
+ * SA_ERR_NULL.  Other arguments, workspace and errors as for the unfused
+ * entry points. */
+sa_status sa_sparse_attn_rope(const uint16_t *q, const uint16_t *kv, const float *sink, const int32_t *idx,
+                              int64_t b, int64_t s, int32_t h, int32_t d, int64_t rows, int32_t topk, float scale,
+                              uint16_t *out, void *workspace, size_t workspace_bytes, void *stream,
+                              int32_t kernel, int32_t splits, const float *rope_table, int64_t n_pos,
+                              int32_t rope_dim, int64_t start_pos);
+
+sa_status sa_sparse_attn_decode_step_rope(const uint16_t *q, uint16_t *kv, const uint16_t *kv_new,
+                                          const float *sink, const int32_t *cidx, int32_t *idx_out, int64_t b,
+                                          int32_t h, int32_t d, int64_t rows, int32_t window, int32_t kc,
+                                          int64_t start_pos, float scale, uint16_t *out, void *workspace,
+                                          size_t workspace_bytes, void *stream, int32_t kernel, int32_t splits,
+                                          const float *rope_table, int64_t n_pos, int32_t rope_dim);
 
 #ifdef __cplusplus
 }

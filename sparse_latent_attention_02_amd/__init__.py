@@ -14,6 +14,8 @@ Names follow the C ABI:
   sparse_attn_decode_step                  -- a whole decode step (ring write, lists, attention) in one launch
   kv8_pack / kv8_unpack                    -- fp8-resident KV rows (e4m3fn codes + E8M0 block scales)
   sparse_attn_kv8 / sparse_attn_decode_step_kv8 -- the attention and the decode step over kv8 rows
+  apply_rotary                             -- rotary embedding of the last rope_dim values (or its inverse)
+  rope= on sparse_attn / sparse_attn_decode_step -- the output's inverse rotation fused into the epilogue
 """
 from __future__ import annotations
 
@@ -73,10 +75,16 @@ def lib() -> ctypes.CDLL:
                                          i32]
         L.sa_sparse_attn_decode_step_kv8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i64, i32, i32,
                                                      i64, f32, vp, vp, sz, vp, i32]
+        L.sa_apply_rotary.argtypes = [vp, i64, i64, i32, i32, i32, vp, i64, i64, i32, vp]
+        L.sa_sparse_attn_rope.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i64, i32, f32, vp, vp, sz, vp,
+                                          i32, i32, vp, i64, i32, i64]
+        L.sa_sparse_attn_decode_step_rope.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i64, i32, i32, i64,
+                                                      f32, vp, vp, sz, vp, i32, i32, vp, i64, i32]
         for fn in ("sa_window_topk_idxs_shape", "sa_window_topk_idxs", "sa_append_compressed_idxs",
                    "sa_act_quant_fp8_inplace", "sa_window_kv_update", "sa_sparse_attn", "sa_sparse_attn_ex",
                    "sa_sparse_attn_decode_step", "sa_kv8_pack", "sa_kv8_unpack", "sa_sparse_attn_kv8",
-                   "sa_sparse_attn_decode_step_kv8"):
+                   "sa_sparse_attn_decode_step_kv8", "sa_apply_rotary", "sa_sparse_attn_rope",
+                   "sa_sparse_attn_decode_step_rope"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -172,10 +180,12 @@ def workspace_bytes(b: int, s: int, h: int, d: int, topk: int, variant: tuple | 
 
 def sparse_attn(q: torch.Tensor, kv: torch.Tensor, sink: torch.Tensor, idx: torch.Tensor, scale: float,
                 out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                variant: tuple | None = None, stream=None) -> torch.Tensor:
+                variant: tuple | None = None, stream=None, rope: tuple | None = None) -> torch.Tensor:
     """q [b][s][h][d] bf16, kv [b][rows][d] bf16, sink [h] f32, idx [b][s][topk] int32 -> [b][s][h][d] bf16.
 
-    ``variant`` = (kernel, splits) forces a kernel variant (see sa_kernel; 0 = automatic)."""
+    ``variant`` = (kernel, splits) forces a kernel variant (see sa_kernel; 0 = automatic).
+    ``rope`` = (table [n_pos][rope_dim/2][2] f32, rope_dim, start_pos) un-rotates the
+    output's last rope_dim values in the epilogue (query s at position start_pos + s)."""
     _dev(q, "q", torch.bfloat16)
     _dev(kv, "kv", torch.bfloat16)
     _dev(sink, "sink", torch.float32)
@@ -198,6 +208,13 @@ def sparse_attn(q: torch.Tensor, kv: torch.Tensor, sink: torch.Tensor, idx: torc
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     args = (q.data_ptr(), kv.data_ptr(), sink.data_ptr(), idx.data_ptr(), b, s, h, d, rows, topk, float(scale),
             out.data_ptr(), ws_ptr, ws_bytes, _stream(stream))
+    if rope is not None:
+        table, rope_dim, start_pos = rope
+        _dev(table, "rope table", torch.float32)
+        k, sp = variant if variant is not None else (0, 0)
+        _check("sa_sparse_attn_rope", lib().sa_sparse_attn_rope(*args, k, sp, table.data_ptr(), table.shape[0],
+                                                                 rope_dim, start_pos))
+        return out
     if variant is None:
         _check("sa_sparse_attn", lib().sa_sparse_attn(*args))
     else:
@@ -214,12 +231,13 @@ def sparse_attn_decode_step(q: torch.Tensor, kv: torch.Tensor, kv_new: torch.Ten
                             window: int, start_pos: int, scale: float, cidx: torch.Tensor | None = None,
                             out: torch.Tensor | None = None, idx_out: torch.Tensor | None = None,
                             workspace: torch.Tensor | None = None, variant: tuple | None = None,
-                            stream=None) -> torch.Tensor:
+                            stream=None, rope: tuple | None = None) -> torch.Tensor:
     """One decode step in one launch: kv_new [b][d] rounded through fp8 into ring slot
     start_pos % window of kv [b][rows][d] (rows [0, window) = ring, compressed rows
     after), the window list + cidx [b][kc] (+window) as the index list, sparse
     attention of q [b][h][d] (or [b][1][h][d]).  kv_new is not modified.  ``idx_out``
-    ([b][window + kc] int32) receives the list when given."""
+    ([b][window + kc] int32) receives the list when given.  ``rope`` = (table,
+    rope_dim) un-rotates the output's last rope_dim values at position start_pos."""
     _dev(q, "q", torch.bfloat16)
     _dev(kv, "kv", torch.bfloat16)
     _dev(kv_new, "kv_new", torch.bfloat16)
@@ -251,12 +269,17 @@ def sparse_attn_decode_step(q: torch.Tensor, kv: torch.Tensor, kv_new: torch.Ten
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check("sa_sparse_attn_decode_step",
-           lib().sa_sparse_attn_decode_step(q.data_ptr(), kv.data_ptr(), kv_new.data_ptr(), sink.data_ptr(),
-                                            cidx.data_ptr() if cidx is not None else None,
-                                            idx_out.data_ptr() if idx_out is not None else None,
-                                            b, h, d, rows, window, kc, start_pos, float(scale), out.data_ptr(),
-                                            ws_ptr, ws_bytes, _stream(stream), k, sp))
+    args = (q.data_ptr(), kv.data_ptr(), kv_new.data_ptr(), sink.data_ptr(),
+            cidx.data_ptr() if cidx is not None else None, idx_out.data_ptr() if idx_out is not None else None,
+            b, h, d, rows, window, kc, start_pos, float(scale), out.data_ptr(), ws_ptr, ws_bytes, _stream(stream),
+            k, sp)
+    if rope is not None:
+        table, rope_dim = rope
+        _dev(table, "rope table", torch.float32)
+        _check("sa_sparse_attn_decode_step_rope",
+               lib().sa_sparse_attn_decode_step_rope(*args, table.data_ptr(), table.shape[0], rope_dim))
+        return out
+    _check("sa_sparse_attn_decode_step", lib().sa_sparse_attn_decode_step(*args))
     return out
 
 
@@ -384,3 +407,19 @@ def sparse_attn_decode_step_kv8(q: torch.Tensor, kv_codes: torch.Tensor, kv_scal
                                                 b, h, d, rows, window, kc, start_pos, float(scale),
                                                 out.data_ptr(), ws_ptr, ws_bytes, _stream(stream), splits))
     return out
+
+
+def apply_rotary(x: torch.Tensor, table: torch.Tensor, rope_dim: int, start_pos: int = 0, inverse: bool = False,
+                 stream=None) -> torch.Tensor:
+    """Rotary embedding of the last ``rope_dim`` values of x [b][s][h][row_len] (or
+    [b][s][row_len]) bf16, in place; row (b, s, .) at position start_pos + s,
+    table [n_pos][rope_dim / 2][2] f32 (cos, sin)."""
+    _dev(x, "x", torch.bfloat16)
+    _dev(table, "table", torch.float32)
+    if x.dim() not in (3, 4):
+        raise ValueError("x must be [b][s][h][row_len] or [b][s][row_len]")
+    b, s = x.shape[0], x.shape[1]
+    h = x.shape[2] if x.dim() == 4 else 1
+    _check("sa_apply_rotary", lib().sa_apply_rotary(x.data_ptr(), b, s, h, x.shape[-1], rope_dim, table.data_ptr(),
+                                                    table.shape[0], start_pos, int(bool(inverse)), _stream(stream)))
+    return x

@@ -90,6 +90,12 @@ struct AttnParams {
     const uint8_t *kv8s;
     uint8_t *kv8c_ring;
     uint8_t *kv8s_ring;
+    // inverse rotation of the output's last rope_dim values (null rope: none):
+    // query (b, s) at position rope_pos0 + s, table [positions][rope_dim / 2] of
+    // (cos, sin) f32
+    const float *rope;
+    int32_t rope_dim;
+    int64_t rope_pos0;
 };
 
 // Entry e of a decode step's concatenated list: the ring listed oldest first,
@@ -117,6 +123,31 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const SA_LDS char *p) {
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Copy of query qi's rotation table row (rope_dim floats, in 16-byte chunks,
+// up to two wave instructions) into LDS at tab; called by one whole wavefront.
+__device__ __forceinline__ void copy_rope_row(const AttnParams &p, uint32_t qi, int lane, uint32_t tab) {
+    const float *row = p.rope + (p.rope_pos0 + (int64_t)(qi % (uint32_t)p.s)) * p.rope_dim;
+    const int chunks = p.rope_dim / 4;
+    if (lane < chunks) dma_16B(row + 4 * lane, tab);
+    if (chunks > 64 && lane < chunks - 64) dma_16B(row + 256 + 4 * lane, tab + 1024);
+}
+
+// The inverse rotation of one 16-byte output chunk (8 rounded bf16 values from
+// d0), if it lies in the last rope_dim values of the row: pair j of the rotated
+// part takes (cos, sin) from tab[2 j], tab[2 j + 1] (the query's table row in
+// LDS).  rope_dim is a multiple of 8, so a chunk lies wholly inside or outside.
+__device__ __forceinline__ u32x4_t unrotate_chunk(u32x4_t v, int d0, int d, int rope_dim, const SA_LDS float *tab) {
+    if (d0 < d - rope_dim) return v;
+    const SA_LDS float *cs = tab + (d0 - (d - rope_dim));
+    const f32x4_t c0 = *reinterpret_cast<const SA_LDS f32x4_t *>(cs);
+    const f32x4_t c1 = *reinterpret_cast<const SA_LDS f32x4_t *>(cs + 4);
+    v[0] = rope_pair(v[0], c0[0], c0[1], true);
+    v[1] = rope_pair(v[1], c0[2], c0[3], true);
+    v[2] = rope_pair(v[2], c1[0], c1[1], true);
+    v[3] = rope_pair(v[3], c1[2], c1[3], true);
+    return v;
+}
 
 // Logical workgroup id.  The dispatcher hands workgroups to the 8 XCDs round
 // robin; the remap gives each XCD a contiguous range of logical ids, so rows
@@ -249,6 +280,7 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
     __shared__ int wcnt[kListCap / 64];
     __shared__ float mlx[2][2][32][2];  // end merge: [head tile][row half][head][max, sum]
     __shared__ int replay[2];
+    __shared__ __attribute__((aligned(16))) float rtab[D];  // the query's rotation table row
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave values in SGPRs
@@ -294,6 +326,10 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
     const int head = ((int)hg * 2 + hw) * 32 + n;
     const bool head_ok = head < p.h;
     const uint32_t smem_base = lds_addr((const SA_LDS void *)smem);
+    // the output rotation's table row for this query, ahead of the head-row copies
+    // (so the wait for those covers it)
+    const bool rot = p.rope != nullptr && p.n_sp == 1;
+    if (rot && wave == 0) copy_rope_row(p, qi, lane, lds_addr((const SA_LDS void *)rtab));
     const SA_LDS char *lds = (const SA_LDS char *)smem;
 
     // the workgroup's 64 head rows of q, copied once into stage buffer 0 (wave w
@@ -583,7 +619,8 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
     for (int hr = wave; hr < C::HEADS; hr += C::NW) {
         const int hglob = (int)hg * C::HEADS + hr;
         if (hglob < p.h && chunk_lane) {
-            const u32x4_t v = *reinterpret_cast<const SA_LDS u32x4_t *>(stg + hr * C::RS + 16 * lane);
+            u32x4_t v = *reinterpret_cast<const SA_LDS u32x4_t *>(stg + hr * C::RS + 16 * lane);
+            if (rot) v = unrotate_chunk(v, 8 * lane, D, p.rope_dim, (const SA_LDS float *)rtab);
             *reinterpret_cast<u32x4_t *>(p.out + ((int64_t)qi * p.h + hglob) * D + lane * 8) = v;
         }
     }
@@ -640,6 +677,7 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) char pbuf[C::HEADS * C::PRS];
     __shared__ float smax[C::NW][16];
     __shared__ float ssum[C::NW][16];
+    __shared__ __attribute__((aligned(16))) float rtab[D];  // the query's rotation table row
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave values in SGPRs
@@ -667,7 +705,8 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
     const bool head_ok = head < p.h;
     // the head's sink, loaded before any copy goes out (a load issued after them
     // would wait behind them at the end)
-    const float sink_h = head_ok ? p.sink[head] : 0.0f;
+    const float sink_h = (head_ok && p.n_sp == 1) ? p.sink[head] : 0.0f;
+    const bool rot = p.rope != nullptr && p.n_sp == 1 && nst > 0;
     const int eoff = C::RPW * wave + (lane & 15);
     auto fetch_stage = [&](int j) -> int {
         const int e = lo + j * C::ROWS + eoff;
@@ -784,6 +823,8 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
     int rowv_nxt = 0;
     if (nst > 0) {
         store_idx(0, v0);
+        // the output rotation's table row for this query (the first stage's wait covers it)
+        if (rot && wave == 0) copy_rope_row(p, qi, lane, lds_addr((const SA_LDS void *)rtab));
         // the query's head rows, once per workgroup: wavefront w copies heads 4w .. 4w+3
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -1016,9 +1057,11 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
     for (int r = 0; r < C::HEADS / C::NW; ++r) {
         const int hr = wave + C::NW * r;
         const int hglob = (int)hg * C::HEADS + hr;
-        if (hglob < p.h && chunk_lane)
-            *reinterpret_cast<u32x4_t *>(p.out + ((int64_t)qi * p.h + hglob) * D + lane * 8) =
-                *reinterpret_cast<const SA_LDS u32x4_t *>((const SA_LDS char *)qbuf + hr * C::RS + 16 * lane);
+        if (hglob < p.h && chunk_lane) {
+            u32x4_t v = *reinterpret_cast<const SA_LDS u32x4_t *>((const SA_LDS char *)qbuf + hr * C::RS + 16 * lane);
+            if (rot) v = unrotate_chunk(v, 8 * lane, D, p.rope_dim, (const SA_LDS float *)rtab);
+            *reinterpret_cast<u32x4_t *>(p.out + ((int64_t)qi * p.h + hglob) * D + lane * 8) = v;
+        }
     }
 }
 
@@ -1030,7 +1073,8 @@ __global__ void __launch_bounds__(256) sa_combine_kernel(const float *__restrict
                                                          const float *__restrict__ part_ml,
                                                          const float *__restrict__ sink,
                                                          uint16_t *__restrict__ out, int64_t nq,
-                                                         int32_t h, int32_t n_sp) {
+                                                         int32_t h, int32_t n_sp, const float *__restrict__ rope,
+                                                         int32_t rope_dim, int64_t rope_pos0, int32_t s_per_seq) {
     constexpr int CPR = D / 8;  // 8-value chunks per row
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= nq * h * CPR) return;
@@ -1057,6 +1101,15 @@ __global__ void __launch_bounds__(256) sa_combine_kernel(const float *__restrict
     const float inv = Lt > 0.f ? 1.0f / Lt : 0.f;
     u32x4_t wv = {pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv),
                   pack_bf16x2(o[4] * inv, o[5] * inv), pack_bf16x2(o[6] * inv, o[7] * inv)};
+    if (rope && c * 8 >= D - rope_dim) {  // the rounded output, un-rotated
+        const float *cs = rope + (rope_pos0 + qi % s_per_seq) * rope_dim + (c * 8 - (D - rope_dim));
+        const f32x4_t c0 = *reinterpret_cast<const f32x4_t *>(cs);
+        const f32x4_t c1 = *reinterpret_cast<const f32x4_t *>(cs + 4);
+        wv[0] = rope_pair(wv[0], c0[0], c0[1], true);
+        wv[1] = rope_pair(wv[1], c0[2], c0[3], true);
+        wv[2] = rope_pair(wv[2], c1[0], c1[1], true);
+        wv[3] = rope_pair(wv[3], c1[2], c1[3], true);
+    }
     *reinterpret_cast<u32x4_t *>(out + qh * D + c * 8) = wv;
 }
 
@@ -1146,7 +1199,8 @@ template <int D>
 hipError_t launch_combine(const AttnParams &p, hipStream_t stream) {
     const int64_t n = (int64_t)p.nq * p.h * (D / 8);
     hipLaunchKernelGGL((sa_combine_kernel<D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                       p.part_o, p.part_ml, p.sink, p.out, (int64_t)p.nq, p.h, p.n_sp);
+                       p.part_o, p.part_ml, p.sink, p.out, (int64_t)p.nq, p.h, p.n_sp, p.rope, p.rope_dim,
+                       p.rope_pos0, p.s);
     return hipGetLastError();
 }
 
@@ -1236,6 +1290,29 @@ struct KvRows {
     }
 };
 
+// The output's inverse rotation (none when table is null): query s of a
+// sequence at position pos0 + s.
+struct Rope {
+    const float *table = nullptr;
+    int64_t n_pos = 0;
+    int32_t dim = 0;
+    int64_t pos0 = 0;
+};
+
+sa_status check_rope(const Rope &r, int32_t d, int64_t s) {
+    if (!r.table) return SA_OK;
+    if (r.dim < 8 || r.dim % 8 != 0 || r.dim > d || r.n_pos < 0 || r.pos0 < 0) return SA_ERR_SHAPE;
+    if (r.pos0 + s > r.n_pos) return SA_ERR_SHAPE;
+    if (reinterpret_cast<uintptr_t>(r.table) % 16) return SA_ERR_SHAPE;
+    return SA_OK;
+}
+
+void set_rope(AttnParams &p, const Rope &r) {
+    p.rope = r.table;
+    p.rope_dim = r.table ? r.dim : 0;
+    p.rope_pos0 = r.pos0;
+}
+
 // kv8 rows are read by the decode kernel only (it walks lists of any length)
 sa_status resolve_variant_kv(int64_t nq, int32_t h, int32_t topk, int32_t kernel, int32_t splits, bool kv8,
                              Variant *out) {
@@ -1246,10 +1323,11 @@ sa_status resolve_variant_kv(int64_t nq, int32_t h, int32_t topk, int32_t kernel
 sa_status run_sparse_attn(const uint16_t *q, const KvRows &kv, const float *sink, const int32_t *idx,
                           int64_t b, int64_t s, int32_t h, int32_t d, int64_t rows, int32_t topk,
                           float scale, uint16_t *out, void *workspace, size_t workspace_bytes,
-                          void *stream, int32_t kernel, int32_t splits) {
+                          void *stream, int32_t kernel, int32_t splits, const Rope &rope = Rope()) {
     if (b < 0 || s < 0 || h < 0 || d < 0 || rows < 0 || topk < 0) return SA_ERR_SHAPE;
     if (!valid_d(d)) return SA_ERR_UNSUPPORTED;
     const int64_t nq = b * s;
+    if (check_rope(rope, d, s) != SA_OK) return SA_ERR_SHAPE;
     if (nq == 0 || h == 0) return SA_OK;
     if (!q || !sink || !out || (topk > 0 && !idx) || (rows > 0 && !kv.present())) return SA_ERR_NULL;
     if (rows > 0x7fffffffLL || nq > 0x7fffffffLL) return SA_ERR_SHAPE;
@@ -1262,6 +1340,7 @@ sa_status run_sparse_attn(const uint16_t *q, const KvRows &kv, const float *sink
     p.kv8c = kv.kc;
     p.kv8s = kv.ks;
     p.idx = idx;
+    set_rope(p, rope);
     return kv.kv8() ? enqueue<false, true>(p, v, d, (hipStream_t)stream)
                     : enqueue<false, false>(p, v, d, (hipStream_t)stream);
 }
@@ -1272,10 +1351,13 @@ sa_status run_sparse_attn(const uint16_t *q, const KvRows &kv, const float *sink
 sa_status run_decode_step(const uint16_t *q, const KvRows &kv, const uint16_t *kv_new, const float *sink,
                           const int32_t *cidx, int32_t *idx_out, int64_t b, int32_t h, int32_t d, int64_t rows,
                           int32_t window, int32_t kc, int64_t start_pos, float scale, uint16_t *out,
-                          void *workspace, size_t workspace_bytes, void *stream, int32_t kernel, int32_t splits) {
+                          void *workspace, size_t workspace_bytes, void *stream, int32_t kernel, int32_t splits,
+                          Rope rope = Rope()) {
     if (b < 0 || h < 0 || d < 0 || rows < 0 || window <= 0 || kc < 0 || start_pos < 0) return SA_ERR_SHAPE;
     if (!valid_d(d)) return SA_ERR_UNSUPPORTED;
     if (start_pos == 0) return SA_ERR_UNSUPPORTED;  // position 0 is a prefill
+    rope.pos0 = start_pos;
+    if (check_rope(rope, d, 1) != SA_OK) return SA_ERR_SHAPE;
     if (rows < window || rows > 0x7fffffffLL || b > 0x7fffffffLL) return SA_ERR_SHAPE;
     if ((int64_t)window + kc > 0x7fffffffLL) return SA_ERR_SHAPE;
     if (b == 0 || h == 0) return SA_OK;
@@ -1302,6 +1384,7 @@ sa_status run_decode_step(const uint16_t *q, const KvRows &kv, const uint16_t *k
     p.kc = kc;
     p.wbase = (int32_t)((start_pos + 1) % window);
     p.new_slot = (int32_t)(start_pos % window);
+    set_rope(p, rope);
     return kv.kv8() ? enqueue<true, true>(p, v, d, (hipStream_t)stream)
                     : enqueue<true, false>(p, v, d, (hipStream_t)stream);
 }
@@ -1395,4 +1478,36 @@ extern "C" sa_status sa_sparse_attn_decode_step_kv8(const uint16_t *q, uint8_t *
                                                     void *stream, int32_t splits) {
     return run_decode_step(q, kv8_rows(kv_codes, kv_scales), kv_new, sink, cidx, idx_out, b, h, d, rows, window,
                            kc, start_pos, scale, out, workspace, workspace_bytes, stream, 0, splits);
+}
+
+extern "C" sa_status sa_sparse_attn_rope(const uint16_t *q, const uint16_t *kv, const float *sink,
+                                         const int32_t *idx, int64_t b, int64_t s, int32_t h, int32_t d,
+                                         int64_t rows, int32_t topk, float scale, uint16_t *out, void *workspace,
+                                         size_t workspace_bytes, void *stream, int32_t kernel, int32_t splits,
+                                         const float *rope_table, int64_t n_pos, int32_t rope_dim,
+                                         int64_t start_pos) {
+    if (!rope_table) return SA_ERR_NULL;
+    Rope r;
+    r.table = rope_table;
+    r.n_pos = n_pos;
+    r.dim = rope_dim;
+    r.pos0 = start_pos;
+    return run_sparse_attn(q, bf16_rows(kv), sink, idx, b, s, h, d, rows, topk, scale, out, workspace,
+                           workspace_bytes, stream, kernel, splits, r);
+}
+
+extern "C" sa_status sa_sparse_attn_decode_step_rope(const uint16_t *q, uint16_t *kv, const uint16_t *kv_new,
+                                                     const float *sink, const int32_t *cidx, int32_t *idx_out,
+                                                     int64_t b, int32_t h, int32_t d, int64_t rows, int32_t window,
+                                                     int32_t kc, int64_t start_pos, float scale, uint16_t *out,
+                                                     void *workspace, size_t workspace_bytes, void *stream,
+                                                     int32_t kernel, int32_t splits, const float *rope_table,
+                                                     int64_t n_pos, int32_t rope_dim) {
+    if (!rope_table) return SA_ERR_NULL;
+    Rope r;
+    r.table = rope_table;
+    r.n_pos = n_pos;
+    r.dim = rope_dim;
+    return run_decode_step(q, bf16_rows(kv), kv_new, sink, cidx, idx_out, b, h, d, rows, window, kc, start_pos,
+                           scale, out, workspace, workspace_bytes, stream, kernel, splits, r);
 }

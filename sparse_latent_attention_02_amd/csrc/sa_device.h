@@ -33,6 +33,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
+// Rotation of one adjacent pair (a, b) of bf16 values, packed with a in the low
+// half, as the complex number a + i b times c + i sn (times c - i sn when
+// inverse) in f32 -- each real product rounded, then the sum (no fused
+// multiply-add) -- rounded back to bf16.
+//   forward: (a c - b sn, a sn + b c)     inverse: (a c + b sn, b c - a sn)
+__device__ __forceinline__ uint32_t rope_pair(uint32_t pk, float c, float sn, bool inverse) {
+#pragma clang fp contract(off)
+    const float a = __uint_as_float(pk << 16), b = __uint_as_float(pk & 0xffff0000u);
+    const float ac = a * c, bs = b * sn, as = a * sn, bc = b * c;
+    const float re = inverse ? ac + bs : ac - bs;
+    const float im = inverse ? bc - as : as + bc;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{re, im}, bf16x2_t));
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const SA_LDS void *p) {
     return (uint32_t)(uintptr_t)p;
 }

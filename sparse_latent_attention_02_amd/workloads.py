@@ -152,3 +152,12 @@ def bf16_bits(t: torch.Tensor):
     """numpy uint16 view of a bf16 CPU tensor's bit patterns."""
     import numpy as np
     return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def rope_table(seed: int, n_pos: int, rope_dim: int) -> torch.Tensor:
+    """A rotation table [n_pos][rope_dim / 2][2] f32 of (cos, sin) pairs at angles
+    drawn uniformly from [-pi, pi): the rotary embedding is defined for any table
+    of unit complex numbers, so random angles stand in for a model's frequencies."""
+    g = torch.Generator().manual_seed(seed)
+    th = (torch.rand((n_pos, rope_dim // 2), generator=g, dtype=torch.float64) * 2 - 1) * torch.pi
+    return torch.stack([torch.cos(th), torch.sin(th)], dim=-1).to(torch.float32).contiguous()

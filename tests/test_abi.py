@@ -102,3 +102,22 @@ def test_kv8_attention_argument_checks(lib):
     assert lib.sa_sparse_attn_kv8_workspace_bytes(64, 1, 64, 512, 128, 0) == 0
     assert lib.sa_sparse_attn_kv8_workspace_bytes(2, 1, 64, 512, 1152, 4) == 2 * 4 * 64 * 514 * 4
     assert lib.sa_sparse_attn_kv8_workspace_bytes(2, 1, 64, 96, 1152, 4) == 0
+
+
+def test_rotary_argument_checks(lib):
+    import sparse_latent_attention_02_amd as sa
+    f = lib.sa_apply_rotary
+    # (x, b, s, h, row_len, rope_dim, table, n_pos, start_pos, inverse, stream)
+    assert f(None, 1, 2, 1, 64, 15, None, 8, 0, 1, None) == sa.SA_ERR_SHAPE      # odd rope_dim
+    assert f(None, 1, 2, 1, 64, 66, None, 8, 0, 1, None) == sa.SA_ERR_SHAPE      # longer than the row
+    assert f(None, 0, 2, 1, 64, 16, None, 8, 0, 1, None) == sa.SA_OK             # empty
+    assert f(None, 1, 2, 1, 64, 16, None, 8, 0, 1, None) == sa.SA_ERR_NULL
+    g = lib.sa_sparse_attn_rope
+    # (q, kv, sink, idx, b, s, h, d, rows, topk, scale, out, ws, ws_bytes, stream, kernel, splits,
+    #  table, n_pos, rope_dim, start_pos)
+    assert g(None, None, None, None, 1, 1, 4, 64, 8, 4, 0.1, None, None, 0, None, 0, 0, None, 8, 16, 0) == \
+        sa.SA_ERR_NULL
+    assert g(None, None, None, None, 1, 4, 4, 64, 8, 4, 0.1, None, None, 0, None, 0, 0, 16, 8, 16, 5) == \
+        sa.SA_ERR_SHAPE                                                             # positions past the table
+    assert g(None, None, None, None, 1, 1, 4, 64, 8, 4, 0.1, None, None, 0, None, 0, 0, 16, 8, 12, 0) == \
+        sa.SA_ERR_SHAPE                                                             # not a multiple of 8
