@@ -10,8 +10,8 @@ Each function follows the page passage cited in ``sa_oracle.c``:
 window selection and the sparse_attn kernel from "DeepSeek V4.1 ... attention /
 attend"; the index concatenation from "... attention / query-latent"
 (Attention.forward, Indexer tail) and the rotary embedding (apply_rotary_emb);
-the ring write, fp8 round trip, pow2_ceil and apply_rotary contract from the
-"Module attn" rustdoc page.
+and the Indexer's selection tail; the ring write, fp8 round trip, pow2_ceil and
+apply_rotary contract from the "Module attn" rustdoc page.
 """
 from __future__ import annotations
 
@@ -64,9 +64,10 @@ def lib() -> ctypes.CDLL:
         L.sao_append_compressed_idxs.argtypes = [vp, i64, i32, vp, i64, i32, i32]
         L.sao_sparse_attn.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i64, i32, f32, vp, vp]
         L.sao_apply_rotary.argtypes = [vp, i64, i64, i32, i32, i32, vp, i64, i64, ctypes.c_int]
+        L.sao_indexer_topk.argtypes = [vp, i64, i64, i32, i64, i32, i32, i32, vp, i64, i32]
         for name in ("sao_window_topk_idxs_shape", "sao_window_topk_idxs", "sao_ring_write",
                      "sao_act_quant_fp8_inplace", "sao_append_compressed_idxs", "sao_sparse_attn",
-                     "sao_kv8_pack", "sao_kv8_unpack", "sao_apply_rotary"):
+                     "sao_kv8_pack", "sao_kv8_unpack", "sao_apply_rotary", "sao_indexer_topk"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -199,3 +200,15 @@ def apply_rotary(x: np.ndarray, table: np.ndarray, rope_dim: int, start_pos: int
     _check("sao_apply_rotary", lib().sao_apply_rotary(_ptr(y), b, s, h, shp[-1], rope_dim, _ptr(t), t.shape[0],
                                                        start_pos, int(bool(inverse))))
     return y
+
+
+def indexer_topk(scores: np.ndarray, start_pos: int, ratio: int, index_topk: int, offset: int) -> np.ndarray:
+    """Indexer selection tail: scores [b][s][T] f32 -> int32 [b][s][min(index_topk, T)]
+    (positions + offset in position order, -1 where unreachable)."""
+    sc = np.ascontiguousarray(scores, dtype=np.float32)
+    b, s, T = sc.shape
+    topk = min(index_topk, T)
+    out = np.full((b, s, topk), -7, dtype=np.int32)
+    _check("sao_indexer_topk", lib().sao_indexer_topk(_ptr(sc), b, s, T, start_pos, ratio, index_topk, offset,
+                                                       _ptr(out), topk, 0))
+    return out

@@ -17,6 +17,8 @@
  *             pow2_ceil, sparse_attn, window_topk_idxs, apply_rotary contracts.
  *   [ROPE]    "DeepSeek V4.1 ... attention / query-latent": apply_rotary_emb
  *             and its use on the attention output (inverse rotation).
+ *   [INDEXER] same page, Indexer.forward: the selection tail (causal
+ *             compress_lens mask, top-k, position order, offset / -1).
  *
  * Arithmetic: sparse_attn in f32 as [ATTN-RS] "Precision" fixes it (f32
  * softmax, bf16 result).  It is written as the plain two-pass softmax
@@ -28,6 +30,7 @@
 #include <math.h>
 #include <stdint.h>
 #include <stddef.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define SAO_OK 0
@@ -432,4 +435,74 @@ int sao_apply_rotary(uint16_t *x, int64_t b, int64_t s, int32_t h, int32_t row_l
             }
         }
     return SAO_OK;
+}
+
+/* ------------------------------------------------ indexer selection tail --- */
+
+typedef struct {
+    float score;
+    int32_t t;
+} sao_cand;
+
+/* best first: larger score, then the lower position */
+static int cand_order(const void *pa, const void *pb) {
+    const sao_cand *a = (const sao_cand *)pa, *b = (const sao_cand *)pb;
+    if (a->score > b->score) return -1;
+    if (a->score < b->score) return 1;
+    return (a->t > b->t) - (a->t < b->t);
+}
+
+static int int_order(const void *pa, const void *pb) {
+    const int32_t a = *(const int32_t *)pa, b = *(const int32_t *)pb;
+    return (a > b) - (a < b);
+}
+
+/* [INDEXER] Indexer.forward, after the scores: with end_pos = start_pos + s and
+ * T = end_pos / ratio compressed positions scored per query (scores
+ * [b][s][T] f32, not NaN):
+ *   compress_lens: prefill (start_pos == 0) query si sees (si + 1) / ratio
+ *     positions and the rest of its row is masked to -inf; otherwise every query
+ *     sees end_pos / ratio (= T) and nothing is masked;
+ *   topk = min(index_topk, T) positions with the largest scores (equal scores:
+ *     the lower position first -- the pages leave the choice open), re-sorted
+ *     into position order;
+ *   out[bi][si][j] = position + offset if position < compress_lens, else -1.
+ * out rows are row_stride apart, entries from column col0 (row_stride >=
+ * col0 + topk).  Integer division is floor division (all operands >= 0). */
+int sao_indexer_topk(const float *scores, int64_t b, int64_t s, int32_t T, int64_t start_pos, int32_t ratio,
+                     int32_t index_topk, int32_t offset, int32_t *out, int64_t row_stride, int32_t col0) {
+    if (b < 0 || s < 0 || T < 0 || start_pos < 0 || ratio <= 0 || index_topk < 0 || offset < 0 || col0 < 0)
+        return SAO_ERR_SHAPE;
+    if ((int64_t)T != (start_pos + s) / ratio) return SAO_ERR_SHAPE;
+    const int32_t topk = index_topk < T ? index_topk : T;
+    if (row_stride < (int64_t)col0 + topk) return SAO_ERR_SHAPE;
+    if (b * s == 0 || topk == 0) return SAO_OK;
+    if (!scores || !out) return SAO_ERR_NULL;
+    for (int64_t e = 0; e < b * s * T; ++e)
+        if (isnan(scores[e])) return SAO_ERR_INDEX;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < b * s; ++r) {
+        const int64_t si = r % s;
+        const int64_t cl = start_pos == 0 ? (si + 1) / ratio : (start_pos + s) / ratio;
+        sao_cand *c = (sao_cand *)malloc(sizeof(sao_cand) * (size_t)T);
+        int32_t *sel = (int32_t *)malloc(sizeof(int32_t) * (size_t)topk);
+        if (!c || !sel) {
+            free(c);
+            free(sel);
+            bad = 1;
+            continue;
+        }
+        for (int32_t t = 0; t < T; ++t) {
+            c[t].score = t >= cl ? -INFINITY : scores[r * T + t];
+            c[t].t = t;
+        }
+        qsort(c, (size_t)T, sizeof(sao_cand), cand_order);
+        for (int32_t j = 0; j < topk; ++j) sel[j] = c[j].t;
+        qsort(sel, (size_t)topk, sizeof(int32_t), int_order);
+        for (int32_t j = 0; j < topk; ++j) out[r * row_stride + col0 + j] = sel[j] < cl ? sel[j] + offset : -1;
+        free(c);
+        free(sel);
+    }
+    return bad ? SAO_ERR_UNSUPPORTED : SAO_OK;
 }

@@ -605,3 +605,77 @@ def test_rotary_shape_errors(oracle_lib):
         with pytest.raises(oracle.OracleError) as e:
             oracle.apply_rotary(x, t, rd, pos, True)
         assert e.value.status == st
+
+
+# --------------------------------------------------- indexer selection tail --
+
+def _torch_tail(scores, start_pos, ratio, index_topk, offset):
+    """The Indexer tail as the page writes it, with torch's own topk/sort/where."""
+    sc = torch.from_numpy(scores.copy())
+    b, s, T = sc.shape
+    end_pos = start_pos + s
+    if start_pos == 0:
+        cl = (torch.arange(1, s + 1) // ratio).unsqueeze(-1)
+        sc.masked_fill_(torch.arange(T) >= cl, -torch.inf)
+    else:
+        cl = end_pos // ratio
+    topk = min(index_topk, end_pos // ratio)
+    idxs = sc.topk(topk, dim=-1, sorted=False).indices.sort(dim=-1).values
+    return torch.where(idxs < cl, idxs + offset, -1).int().numpy()
+
+
+@pytest.mark.parametrize("b,s,start_pos,ratio,index_topk,offset", [
+    (3, 1, 4999, 4, 512, 128),       # decode: T = 1250, no mask
+    (2, 1, 65535, 4, 2048, 128),     # decode: T = 16384
+    (1, 64, 0, 4, 8, 8192),          # prefill: causal compress_lens mask, -1 past it
+    (1, 200, 0, 4, 2048, 8192),      # prefill, topk past T: everything, in order
+    (2, 3, 40, 2, 7, 5),             # a chunk after position 0: one compress_lens for all
+])
+def test_indexer_tail_matches_torch_topk(oracle_lib, b, s, start_pos, ratio, index_topk, offset):
+    """Distinct finite scores: the selected set is unique, and must be exactly
+    torch.topk's, re-sorted and mapped as the page does."""
+    g = torch.Generator().manual_seed(b * 1000 + s + start_pos)
+    T = (start_pos + s) // ratio
+    sc = torch.randn((b, s, T), generator=g, dtype=torch.float32).numpy()
+    got = oracle.indexer_topk(sc, start_pos, ratio, index_topk, offset)
+    assert np.array_equal(got, _torch_tail(sc, start_pos, ratio, index_topk, offset))
+
+
+def test_indexer_tail_prefill_counts_and_order(oracle_lib):
+    g = torch.Generator().manual_seed(5)
+    s, ratio, topk, off = 96, 4, 10, 300
+    sc = torch.randn((1, s, s // ratio), generator=g).numpy()
+    got = oracle.indexer_topk(sc, 0, ratio, topk, off)[0]
+    for si in range(s):
+        cl = (si + 1) // ratio
+        row = got[si]
+        valid = row[row >= 0]
+        assert len(valid) == min(topk, cl)
+        assert np.all(valid >= off) and np.all(valid < off + cl)
+        assert np.all(np.diff(valid) > 0)                       # position order
+        assert np.all(row[len(valid):] == -1)                   # -1 entries last
+        best = np.sort(np.argsort(-sc[0, si, :cl], kind="stable")[:min(topk, cl)]) + off
+        assert np.array_equal(valid, best)
+
+
+def test_indexer_tail_ties_take_the_lower_position(oracle_lib):
+    """Equal scores: the pages leave the choice open; the oracle (and the GPU
+    kernel) take the lower position first."""
+    sc = np.zeros((1, 1, 40), dtype=np.float32)
+    assert np.array_equal(oracle.indexer_topk(sc, 159, 4, 6, 10)[0, 0], np.arange(6) + 10)
+    sc[0, 0, [3, 17, 30]] = 1.0                                  # three winners, then ties at 0
+    assert np.array_equal(oracle.indexer_topk(sc, 159, 4, 5, 0)[0, 0], [0, 1, 3, 17, 30])
+    sc[0, 0, 5] = -np.inf
+    assert 5 not in oracle.indexer_topk(sc, 159, 4, 39, 0)[0, 0]
+
+
+def test_indexer_tail_rejects_bad_shapes(oracle_lib):
+    sc = np.zeros((1, 1, 10), dtype=np.float32)
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.indexer_topk(sc, 50, 4, 4, 0)                    # T must be end_pos // ratio
+    assert e.value.status == oracle.ERR_SHAPE
+    sc = np.zeros((1, 1, 10), dtype=np.float32)
+    sc[0, 0, 2] = np.nan
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.indexer_topk(sc, 40, 4, 4, 0)
+    assert e.value.status == oracle.ERR_INDEX
