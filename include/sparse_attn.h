@@ -14,6 +14,7 @@
  *             apply_rotary.
  *   [ROPE]    "DeepSeek V4.1 ... attention / query-latent" -- apply_rotary_emb
  *             and the inverse rotation of the attention output.
+ *   [INDEXER] same page, Indexer.forward -- the selection tail.
  *
  * Conventions for every entry point:
  *   - bf16 tensors are passed as uint16_t bit patterns; f32 as float.
@@ -362,6 +363,28 @@ sa_status sa_sparse_attn_decode_step_rope(const uint16_t *q, uint16_t *kv, const
                                           int64_t start_pos, float scale, uint16_t *out, void *workspace,
                                           size_t workspace_bytes, void *stream, int32_t kernel, int32_t splits,
                                           const float *rope_table, int64_t n_pos, int32_t rope_dim);
+
+/* ------------------------------------------------------------------------
+ * The indexer's selection tail -- [INDEXER] Indexer.forward after the scores
+ * (the compressed half of the index list).
+ *
+ *   scores [b][s][n_cols] f32   index scores of the n_cols = (start_pos + s) /
+ *                               ratio compressed positions (else SA_ERR_SHAPE);
+ *                               not NaN (a NaN ranks above +inf, undefined by
+ *                               the pages)
+ *   idx    int32, rows of row_stride entries, one per (b, s) query; the
+ *          selection goes to columns [col0, col0 + topk) and nothing else is
+ *          written (row_stride >= col0 + topk, else SA_ERR_SHAPE)
+ * For query (bi, si): compress_lens = (si + 1) / ratio when start_pos == 0
+ * (positions past it are masked to -inf), else (start_pos + s) / ratio;
+ * topk = min(index_topk, n_cols) positions with the largest scores (equal
+ * scores: the lower position first -- the pages leave the choice open) are
+ * listed in position order as position + offset, or -1 where the position is
+ * >= compress_lens.  Deterministic; bit-exact against that definition.
+ * ratio >= 1, offset >= 0, col0 >= 0 (else SA_ERR_SHAPE). */
+sa_status sa_indexer_topk(const float *scores, int64_t b, int64_t s, int32_t n_cols, int64_t start_pos,
+                          int32_t ratio, int32_t index_topk, int32_t offset, int32_t *idx, int64_t row_stride,
+                          int32_t col0, void *stream);
 
 #ifdef __cplusplus
 }

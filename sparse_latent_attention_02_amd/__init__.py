@@ -16,6 +16,7 @@ Names follow the C ABI:
   sparse_attn_kv8 / sparse_attn_decode_step_kv8 -- the attention and the decode step over kv8 rows
   apply_rotary                             -- rotary embedding of the last rope_dim values (or its inverse)
   rope= on sparse_attn / sparse_attn_decode_step -- the output's inverse rotation fused into the epilogue
+  indexer_topk                             -- the indexer's selection tail (compressed positions of the list)
 """
 from __future__ import annotations
 
@@ -80,11 +81,12 @@ def lib() -> ctypes.CDLL:
                                           i32, i32, vp, i64, i32, i64]
         L.sa_sparse_attn_decode_step_rope.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i64, i32, i32, i64,
                                                       f32, vp, vp, sz, vp, i32, i32, vp, i64, i32]
+        L.sa_indexer_topk.argtypes = [vp, i64, i64, i32, i64, i32, i32, i32, vp, i64, i32, vp]
         for fn in ("sa_window_topk_idxs_shape", "sa_window_topk_idxs", "sa_append_compressed_idxs",
                    "sa_act_quant_fp8_inplace", "sa_window_kv_update", "sa_sparse_attn", "sa_sparse_attn_ex",
                    "sa_sparse_attn_decode_step", "sa_kv8_pack", "sa_kv8_unpack", "sa_sparse_attn_kv8",
                    "sa_sparse_attn_decode_step_kv8", "sa_apply_rotary", "sa_sparse_attn_rope",
-                   "sa_sparse_attn_decode_step_rope"):
+                   "sa_sparse_attn_decode_step_rope", "sa_indexer_topk"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -423,3 +425,23 @@ def apply_rotary(x: torch.Tensor, table: torch.Tensor, rope_dim: int, start_pos:
     _check("sa_apply_rotary", lib().sa_apply_rotary(x.data_ptr(), b, s, h, x.shape[-1], rope_dim, table.data_ptr(),
                                                     table.shape[0], start_pos, int(bool(inverse)), _stream(stream)))
     return x
+
+
+def indexer_topk(scores: torch.Tensor, start_pos: int, ratio: int, index_topk: int, offset: int,
+                 out: torch.Tensor | None = None, col0: int = 0, stream=None) -> torch.Tensor:
+    """Indexer selection tail: scores [b][s][T] f32 (T = (start_pos + s) // ratio) ->
+    int32 [b][s][min(index_topk, T)] positions + offset in position order, -1 where
+    unreachable.  With ``out`` ([b][s][cols] int32) the selection is written into
+    columns [col0, col0 + topk) of it (e.g. after the window columns)."""
+    _dev(scores, "scores", torch.float32)
+    b, s, T = scores.shape
+    topk = min(index_topk, T)
+    if out is None:
+        out = torch.empty((b, s, topk), dtype=torch.int32, device=scores.device)
+        col0 = 0
+    _dev(out, "out", torch.int32)
+    if out.dim() != 3 or out.shape[0] != b or out.shape[1] != s:
+        raise ValueError(f"out must be [{b}][{s}][cols]")
+    _check("sa_indexer_topk", lib().sa_indexer_topk(scores.data_ptr(), b, s, T, start_pos, ratio, index_topk,
+                                                    offset, out.data_ptr(), out.shape[2], col0, _stream(stream)))
+    return out

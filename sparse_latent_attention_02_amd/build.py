@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsparse_attn.so")
-SOURCES = ["sa_index.hip", "sa_quant.hip", "sa_rope.hip", "sa_attn.hip"]
+SOURCES = ["sa_index.hip", "sa_quant.hip", "sa_rope.hip", "sa_select.hip", "sa_attn.hip"]
 ARCH = "gfx950"
 
 

@@ -1,0 +1,192 @@
+// sa_select.hip -- the indexer's selection tail on the GPU.
+//
+// "DeepSeek V4.1 ... attention / query-latent", Indexer.forward after the
+// scores: the causal compress_lens mask (prefill), the top-k positions by score,
+// re-sorted into position order, shifted by the offset, -1 where unreachable.
+// Equal scores: the lower position first (the pages leave the choice open).
+//
+// One workgroup per query row.  The k-th largest score is found by a radix
+// select over order-preserving 32-bit keys (four 8-bit digits, most significant
+// first: a histogram of the keys that match the digits fixed so far, then the
+// digit where the count from the top reaches the number still to take).  A
+// last pass over the row in position order keeps the keys above that threshold
+// and the first few equal to it, with a workgroup prefix sum giving each kept
+// position its output column -- so the output comes out in position order with
+// no sort.  Rows of up to kKeyCap positions keep their keys in LDS; longer rows
+// are re-read from memory in each pass.
+#include "sa_device.h"
+#include "../../include/sparse_attn.h"
+
+namespace {
+
+using namespace sa;
+
+constexpr int kSelThreads = 256;
+constexpr int kKeyCap = 16384;  // keys held in LDS (64 KiB)
+constexpr int kPerThread = 4;   // consecutive positions per thread in the ordered pass
+
+// f32 -> u32 with the same order (larger value, larger key); -inf is the
+// smallest non-NaN key, and a masked position takes that key.
+__device__ __forceinline__ uint32_t order_key(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+constexpr uint32_t kKeyNegInf = 0x007fffffu;  // order_key(-inf)
+
+// Exclusive prefix sum over the workgroup of v (each thread's value); the total
+// goes to *total.  Uses sums[4] in LDS; all threads call it.
+__device__ __forceinline__ uint32_t wg_exclusive_sum(uint32_t v, uint32_t *sums, uint32_t *total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) sums[wave] = x;
+    __syncthreads();
+    uint32_t before = 0;
+#pragma unroll
+    for (int w = 0; w < kSelThreads / 64; ++w)
+        if (w < wave) before += sums[w];
+    *total = sums[0] + sums[1] + sums[2] + sums[3];
+    __syncthreads();  // sums may be reused by the next call
+    return before + x - v;
+}
+
+template <bool CACHED>
+__global__ void __launch_bounds__(kSelThreads) indexer_topk_kernel(const float *__restrict__ scores, int64_t s,
+                                                                   int32_t T, int64_t start_pos, int32_t ratio,
+                                                                   int32_t topk, int32_t offset,
+                                                                   int32_t *__restrict__ out, int64_t row_stride,
+                                                                   int32_t col0) {
+    __shared__ uint32_t keys[CACHED ? kKeyCap : 1];
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t sums[4];
+    __shared__ uint32_t pick[2];  // digit, count of matching keys above it
+
+    const int tid = threadIdx.x;
+    const int64_t r = blockIdx.x;
+    const int64_t si = r % s;
+    const int64_t cl = start_pos == 0 ? (si + 1) / ratio : (start_pos + s) / ratio;  // compress_lens
+    const float *sr = scores + r * T;
+    int32_t *orow = out + r * row_stride + col0;
+    auto key_of = [&](int t) -> uint32_t {
+        if (CACHED) return keys[t];
+        return t < cl ? order_key(sr[t]) : kKeyNegInf;
+    };
+
+    if (topk >= T) {  // every position is taken
+        for (int t = tid; t < T; t += kSelThreads) orow[t] = t < cl ? t + offset : -1;
+        return;
+    }
+    if (CACHED) {
+        for (int t = tid; t < T; t += kSelThreads) keys[t] = t < cl ? order_key(sr[t]) : kKeyNegInf;
+    }
+
+    // ---- radix select of the threshold key: topk-th largest ----
+    uint32_t prefix = 0, pmask = 0;
+    uint32_t need = (uint32_t)topk;  // how many keys matching the prefix are still to take
+#pragma unroll 1
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        hist[tid] = 0;  // (kSelThreads == 256 bins)
+        __syncthreads();
+        for (int t = tid; t < T; t += kSelThreads) {
+            const uint32_t k = key_of(t);
+            if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (tid < 64) {
+            // lane l holds bins 4 l .. 4 l + 3; suffix sums from the top bin down
+            const uint32_t h0 = hist[4 * tid], h1 = hist[4 * tid + 1], h2 = hist[4 * tid + 2], h3 = hist[4 * tid + 3];
+            const uint32_t c = h0 + h1 + h2 + h3;
+            uint32_t sfx = c;  // sum over lanes >= this one
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t y = __shfl_down(sfx, o, 64);
+                if (tid + o < 64) sfx += y;
+            }
+            const uint64_t ok = __ballot(sfx >= need);  // lane 0 always qualifies
+            const int L = 63 - __builtin_clzll(ok);     // highest lane whose suffix reaches need
+            if (tid == L) {
+                uint32_t cum = sfx - c;                 // keys in bins above this lane's
+                const uint32_t hb[4] = {h0, h1, h2, h3};
+                int digit = 4 * L;
+                for (int j = 3; j >= 0; --j) {
+                    if (cum + hb[j] >= need) {
+                        digit = 4 * L + j;
+                        break;
+                    }
+                    cum += hb[j];
+                }
+                pick[0] = (uint32_t)digit;
+                pick[1] = cum;
+            }
+        }
+        __syncthreads();
+        prefix |= pick[0] << shift;
+        pmask |= 255u << shift;
+        need -= pick[1];
+        __syncthreads();  // pick and hist are rewritten by the next pass
+    }
+    const uint32_t thr = prefix;  // keys above are all taken, `need` of those equal to it
+
+    // ---- ordered pass: positions in order, 4 consecutive per thread ----
+    uint32_t written = 0, eq_left = need;
+    for (int base = 0; base < T; base += kSelThreads * kPerThread) {
+        const int t0 = base + kPerThread * tid;
+        uint32_t kk[kPerThread];
+        uint32_t n_gt = 0, n_eq = 0;
+#pragma unroll
+        for (int j = 0; j < kPerThread; ++j) {
+            kk[j] = t0 + j < T ? key_of(t0 + j) : 0u;
+            n_gt += (t0 + j < T && kk[j] > thr) ? 1u : 0u;
+            n_eq += (t0 + j < T && kk[j] == thr) ? 1u : 0u;
+        }
+        // (at most kSelThreads * kPerThread = 1024 per tile: two 16-bit counts in one word)
+        uint32_t tot;
+        const uint32_t pre = wg_exclusive_sum(n_gt | (n_eq << 16), sums, &tot);
+        const uint32_t gt_before = pre & 0xffffu, eq_before = pre >> 16;
+        // equal keys are taken in position order while their rank among the equal
+        // keys still to take is below eq_left
+        uint32_t pos = written + gt_before + min(eq_before, eq_left);
+        uint32_t eq_rank = eq_before;
+#pragma unroll
+        for (int j = 0; j < kPerThread; ++j) {
+            const int t = t0 + j;
+            if (t >= T) break;
+            bool take = kk[j] > thr;
+            if (kk[j] == thr) take = eq_rank++ < eq_left;
+            if (take && pos < (uint32_t)topk) orow[pos++] = t < cl ? t + offset : -1;
+        }
+        const uint32_t tile_eq = tot >> 16;
+        const uint32_t tile_eq_taken = min(tile_eq, eq_left);
+        written += (tot & 0xffffu) + tile_eq_taken;
+        eq_left -= tile_eq_taken;
+    }
+}
+
+}  // namespace
+
+extern "C" sa_status sa_indexer_topk(const float *scores, int64_t b, int64_t s, int32_t n_cols, int64_t start_pos,
+                                     int32_t ratio, int32_t index_topk, int32_t offset, int32_t *idx,
+                                     int64_t row_stride, int32_t col0, void *stream) {
+    if (b < 0 || s < 0 || n_cols < 0 || start_pos < 0 || ratio <= 0 || index_topk < 0 || offset < 0 || col0 < 0)
+        return SA_ERR_SHAPE;
+    if ((int64_t)n_cols != (start_pos + s) / ratio) return SA_ERR_SHAPE;
+    const int32_t topk = index_topk < n_cols ? index_topk : n_cols;
+    if (row_stride < (int64_t)col0 + topk) return SA_ERR_SHAPE;
+    const int64_t rows = b * s;
+    if (rows == 0 || topk == 0) return SA_OK;
+    if (!scores || !idx) return SA_ERR_NULL;
+    if (rows > 0x7fffffffLL) return SA_ERR_SHAPE;
+    if (n_cols <= kKeyCap)
+        hipLaunchKernelGGL(indexer_topk_kernel<true>, dim3((unsigned)rows), dim3(kSelThreads), 0,
+                           (hipStream_t)stream, scores, s, n_cols, start_pos, ratio, topk, offset, idx, row_stride,
+                           col0);
+    else
+        hipLaunchKernelGGL(indexer_topk_kernel<false>, dim3((unsigned)rows), dim3(kSelThreads), 0,
+                           (hipStream_t)stream, scores, s, n_cols, start_pos, ratio, topk, offset, idx, row_stride,
+                           col0);
+    return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
+}

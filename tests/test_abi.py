@@ -121,3 +121,14 @@ def test_rotary_argument_checks(lib):
         sa.SA_ERR_SHAPE                                                             # positions past the table
     assert g(None, None, None, None, 1, 1, 4, 64, 8, 4, 0.1, None, None, 0, None, 0, 0, 16, 8, 12, 0) == \
         sa.SA_ERR_SHAPE                                                             # not a multiple of 8
+
+
+def test_indexer_topk_argument_checks(lib):
+    import sparse_latent_attention_02_amd as sa
+    f = lib.sa_indexer_topk
+    # (scores, b, s, n_cols, start_pos, ratio, index_topk, offset, idx, row_stride, col0, stream)
+    assert f(None, 1, 1, 10, 50, 4, 4, 0, None, 4, 0, None) == sa.SA_ERR_SHAPE      # n_cols != end_pos // ratio
+    assert f(None, 1, 1, 10, 40, 0, 4, 0, None, 4, 0, None) == sa.SA_ERR_SHAPE      # ratio 0
+    assert f(None, 1, 1, 10, 40, 4, 4, 0, None, 3, 0, None) == sa.SA_ERR_SHAPE      # row narrower than topk
+    assert f(None, 0, 1, 10, 40, 4, 4, 0, None, 4, 0, None) == sa.SA_OK             # no rows
+    assert f(None, 1, 1, 10, 40, 4, 4, 0, None, 4, 0, None) == sa.SA_ERR_NULL

@@ -1,0 +1,80 @@
+"""GPU parity of the indexer's selection tail (sa_indexer_topk): bit for bit
+against the oracle (both take equal scores at the lower position first), on
+decode rows short enough for LDS and longer ones, causal prefill masks, the
+take-everything case, heavy ties, -inf scores, and writes into the compressed
+columns of a wider index buffer (other columns untouched)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_latent_attention_02_amd as sa
+from helpers import require_gpu
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    sa.lib()
+    oracle.lib()
+
+
+CASES = [
+    # (seed, b, s, start_pos, ratio, index_topk, offset, score kind)
+    (1, 128, 1, 65535, 4, 2048, 128, "normal"),    # decode: 16384 positions (keys in LDS)
+    (2, 8, 1, 131071, 4, 2048, 128, "normal"),     # decode: 32768 positions (re-read from memory)
+    (3, 1, 2048, 0, 4, 100, 2048, "normal"),       # prefill: causal mask, -inf ties past compress_lens
+    (4, 1, 8192, 0, 4, 2048, 8192, "normal"),      # prefill: topk = T, everything in order
+    (5, 16, 1, 40000, 4, 700, 128, "ties"),        # few distinct values: ties at the threshold
+    (6, 4, 1, 20000, 4, 300, 0, "neginf"),         # -inf scores among finite ones
+    (7, 3, 5, 77, 3, 9, 17, "normal"),             # a chunk after position 0
+    (8, 2, 1, 4095, 1, 4096, 5, "ties"),           # ratio 1, topk = T
+]
+
+
+def make_scores(seed, b, s, T, kind):
+    g = torch.Generator().manual_seed(seed)
+    if kind == "ties":
+        return torch.randint(0, 4, (b, s, T), generator=g).to(torch.float32)
+    sc = torch.randn((b, s, T), generator=g)
+    if kind == "neginf":
+        sc[torch.rand((b, s, T), generator=g) < 0.3] = -torch.inf
+    return sc
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"case{c[0]}" for c in CASES])
+def test_indexer_topk_vs_oracle(case):
+    seed, b, s, start_pos, ratio, index_topk, offset, kind = case
+    T = (start_pos + s) // ratio
+    print(f"indexer tail case {case} T={T}", flush=True)
+    sc = make_scores(seed, b, s, T, kind)
+    ref = oracle.indexer_topk(sc.numpy(), start_pos, ratio, index_topk, offset)
+    got = sa.indexer_topk(sc.to(DEV), start_pos, ratio, index_topk, offset)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), ref)
+
+
+def test_indexer_topk_into_the_compressed_columns():
+    b, s, start_pos, ratio, topk, W = 4, 1, 9999, 4, 512, 128
+    T = (start_pos + s) // ratio
+    sc = make_scores(11, b, s, T, "normal")
+    buf = torch.full((b, s, W + topk + 3), -9, dtype=torch.int32, device=DEV)
+    sa.indexer_topk(sc.to(DEV), start_pos, ratio, topk, W, out=buf, col0=W)
+    torch.cuda.synchronize()
+    got = buf.cpu().numpy()
+    assert np.all(got[..., :W] == -9) and np.all(got[..., W + topk:] == -9)
+    assert np.array_equal(got[..., W:W + topk], oracle.indexer_topk(sc.numpy(), start_pos, ratio, topk, W))
+
+
+def test_indexer_topk_errors():
+    sc = torch.zeros((1, 1, 10), device=DEV)
+    with pytest.raises(sa.SparseAttnError) as e:
+        sa.indexer_topk(sc, 50, 4, 4, 0)                     # T != (start_pos + s) // ratio
+    assert e.value.status == sa.SA_ERR_SHAPE
+    out = torch.zeros((1, 1, 3), dtype=torch.int32, device=DEV)
+    with pytest.raises(sa.SparseAttnError) as e:
+        sa.indexer_topk(sc, 40, 4, 4, 0, out=out)            # buffer narrower than topk
+    assert e.value.status == sa.SA_ERR_SHAPE
