@@ -9,7 +9,9 @@ workloads run the step as one launch (sa_sparse_attn_decode_step, the lists
 built inside the attention kernel); ``--unfused`` times the separate calls.
 ``--kv8`` holds the decode cache fp8-resident (e4m3fn codes + E8M0 block
 scales) and runs the one-launch step on it: the same results, bit for bit,
-from about half the gathered bytes.
+from about half the gathered bytes.  ``--rope`` fuses the output's inverse
+rotary embedding into the epilogue.  ``--select`` measures the indexer's
+selection tail on its own workload instead (one JSON line of its own).
 
 Default workload: decode over the window ring, batch 64 single-query steps at
 position 5000, 64 heads, head dim 512, 128-slot ring (the configuration the
@@ -63,6 +65,10 @@ def parse():
     ap.add_argument("--kv8", action="store_true",
                     help="decode: the cache held fp8-resident (e4m3fn codes + E8M0 block scales) and read "
                          "and written in that form by the one-launch step (bitwise the same results)")
+    ap.add_argument("--rope", action="store_true",
+                    help="fuse the output's inverse rotary embedding (last 64 values) into the attention epilogue")
+    ap.add_argument("--select", action="store_true",
+                    help="measure the indexer selection tail (sa_indexer_topk) on its workload instead")
     ap.add_argument("--no-graphs", dest="graphs", action="store_false",
                     help="launch every step eagerly from Python instead of replaying HIP graphs")
     return ap.parse_args()
@@ -102,15 +108,18 @@ def algorithmic_work(w, idx_sets, fused=False, kv8=False):
 
 
 def source_sha():
+    """Hash of every kernel source: a counter summary taken on other sources is stale."""
     h = hashlib.sha256()
-    for f in ("sa_attn.hip", "sa_device.h", "sa_fp8.h"):
-        with open(os.path.join(HERE, "sparse_latent_attention_02_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    csrc = os.path.join(HERE, "sparse_latent_attention_02_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
-def traffic_tag(wid, fused, kv8):
-    return f"w{wid}{'_kv8' if kv8 else ''}{'' if fused else '_unfused'}"
+def traffic_tag(wid, fused, kv8, rope_dim=0):
+    return f"w{wid}{'_kv8' if kv8 else ''}{'_rope' if rope_dim else ''}{'' if fused else '_unfused'}"
 
 
 def measured_traffic(tag):
@@ -216,6 +225,91 @@ def cpu_baseline(wid, target_s):
                       f"attention); {t:.2f} s"}
 
 
+def copy_calibration():
+    """A plain streaming copy of known size (1 GiB read, 1 GiB written) with the
+    same 16-byte-per-lane access width as the kernels, for scaling the HBM byte
+    counters of a rocprofv3 run."""
+    import torch
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def bench_select(args):
+    """The indexer selection tail on its workload (decode, 128 queries x 16384
+    scored compressed positions, top 2048): HBM bound -- the scores are read and
+    the selected columns written once (the radix passes re-read the row from
+    LDS)."""
+    import torch
+    import numpy as np
+    import sparse_latent_attention_02_amd as sa
+    from sparse_latent_attention_02_amd import workloads as wl
+    cfg = wl.SELECT_WORKLOAD
+    b, s, start_pos, ratio = cfg["b"], cfg["s"], cfg["start_pos"], cfg["ratio"]
+    T = (start_pos + s) // ratio
+    topk = min(cfg["index_topk"], T)
+    win = cfg["offset"]
+    bytes_per = b * s * T * 4 + b * s * topk * 4
+    n_sets = args.sets or max(1, min(96, math.ceil(2 * MALL_BYTES / bytes_per)))
+    scores = [wl.indexer_scores(3000 + k, b, s, T).cuda() for k in range(n_sets)]
+    outs = [torch.empty((b, s, win + topk), dtype=torch.int32, device="cuda") for _ in range(n_sets)]
+    call = lambda i: sa.indexer_topk(scores[i], start_pos, ratio, cfg["index_topk"], win, out=outs[i], col0=win)
+    if args.copy_calibration:
+        copy_calibration()
+    for i in range(args.warmup):
+        call(i % n_sets)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n_sets):
+            call(i)
+    reps = max(1, math.ceil(args.steps / n_sets))
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    n = reps * n_sets
+    ms = e0.elapsed_time(e1) / n
+    achieved = bytes_per / (ms / 1e3) / 1e9
+    line = {
+        "metric": "indexer_topk query rows/s", "value": round(b * s / (ms / 1e3), 1), "unit": "rows/s",
+        "n_gpus": 1, "steps": n, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"indexer selection tail: b={b} decode at position {start_pos}, ratio {ratio}, "
+                               f"{T} scored positions, top {topk}, offset {win}",
+                   "input_sets": n_sets, "launch": f"hip graph of {n_sets} calls", "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic("select"),
+                     "algorithmic_bytes": bytes_per, "kernel_ms_mean": round(ms, 5), "kernel_launches_timed": n},
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+        sc = wl.indexer_scores(3000, b, s, T).numpy()
+        t0 = time.perf_counter()
+        passes = 0
+        while True:
+            oracle.indexer_topk(sc, start_pos, ratio, cfg["index_topk"], win)
+            passes += 1
+            el = time.perf_counter() - t0
+            if el > args.cpu_seconds or passes >= 1000:
+                break
+        line["cpu_baseline"] = {"value": round(passes * b * s / el, 1), "unit": "rows/s", "cores": threads,
+                                "kind": "oracle", "sample": f"input set 0 ({b} rows), {passes} passes; {el:.2f} s"}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -233,6 +327,9 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     sa.lib()
+    if args.select:
+        bench_select(args)
+        return
     w = wl.WORKLOADS[args.workload]
 
     # ---- inputs resident in HBM, rotating sets for small workloads ----
@@ -240,7 +337,11 @@ def main():
     if args.kv8 and (w.start_pos == 0 or args.unfused):
         print("bench.py: --kv8 applies to the one-launch decode step (workloads 2 and 4)", file=sys.stderr)
         sys.exit(2)
-    sets = [pipeline.prepare(args.workload, raw0, kv8=args.kv8)]
+    rope_dim = pipeline.ROPE_DIM if args.rope else 0
+    if args.rope and args.kv8:
+        print("bench.py: --rope and --kv8 are not combined", file=sys.stderr)
+        sys.exit(2)
+    sets = [pipeline.prepare(args.workload, raw0, kv8=args.kv8, rope_dim=rope_dim)]
     pipeline.build_index(sets[0])
     torch.cuda.synchronize()
     fused = w.start_pos > 0 and not args.unfused
@@ -250,22 +351,17 @@ def main():
         step_fn = pipeline.step_fused if fused else pipeline.step
         kern_fn = pipeline.step_fused if fused else pipeline.attend    # the dominant kernel's launch
     work = algorithmic_work(w, [sets[0].idx], fused, args.kv8)
+    if rope_dim:
+        work["bytes"] += w.b * w.s * rope_dim * 4       # each query's table row
     n_sets = args.sets or max(1, min(48, math.ceil(2 * MALL_BYTES / work["bytes"])))
     for k in range(1, n_sets):
-        sets.append(pipeline.prepare(args.workload, wl.generate(args.workload, seed_offset=97 * k), kv8=args.kv8))
+        sets.append(pipeline.prepare(args.workload, wl.generate(args.workload, seed_offset=97 * k), kv8=args.kv8,
+                                     rope_dim=rope_dim))
     del raw0
     torch.cuda.synchronize()
 
     if args.copy_calibration:
-        # a plain streaming copy of known size (1 GiB read, 1 GiB written) with the
-        # same 16-byte-per-lane access width as the attention kernels, for scaling
-        # the HBM byte counters
-        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration()
 
     # ---- warmup (eager), then one HIP graph per input set for the step and for
     #      the attention launch alone: replays keep the host out of the timing ----
@@ -342,7 +438,7 @@ def main():
         achieved = work["flops"] / (attn_mean / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
-    roof["traffic"] = measured_traffic(traffic_tag(args.workload, fused or w.start_pos == 0, args.kv8))
+    roof["traffic"] = measured_traffic(traffic_tag(args.workload, fused or w.start_pos == 0, args.kv8, rope_dim))
     roof["algorithmic_bytes"] = work["bytes"]
     roof["algorithmic_flops"] = work["flops"]
     roof["kernel_ms_mean"] = round(attn_mean, 5)
@@ -366,6 +462,8 @@ def main():
                    "input_sets": n_sets, "launch": launch_desc,
                    "step": "one-launch decode step" if fused else "separate calls",
                    "kv_cache": "fp8 e4m3fn codes + E8M0 block scales" if args.kv8 else "bf16",
+                   "output_rotation": f"inverse rotary embedding of the last {rope_dim} values, fused"
+                   if rope_dim else "none",
                    "parallelism": "single GPU"},
         "roofline": roof,
         "wall_s": round(wall, 3),

@@ -6,9 +6,10 @@
 // Equal scores: the lower position first (the pages leave the choice open).
 //
 // One workgroup per query row.  The k-th largest score is found by a radix
-// select over order-preserving 32-bit keys (four 8-bit digits, most significant
-// first: a histogram of the keys that match the digits fixed so far, then the
-// digit where the count from the top reaches the number still to take).  A
+// select over order-preserving 32-bit keys (digits of 12, 10 and 10 bits, most
+// significant first: a histogram of the keys that match the digits fixed so
+// far, then the digit where the count from the top reaches the number still to
+// take).  A
 // last pass over the row in position order keeps the keys above that threshold
 // and the first few equal to it, with a workgroup prefix sum giving each kept
 // position its output column -- so the output comes out in position order with
@@ -21,9 +22,10 @@ namespace {
 
 using namespace sa;
 
-constexpr int kSelThreads = 256;
+constexpr int kSelThreads = 1024;
 constexpr int kKeyCap = 16384;  // keys held in LDS (64 KiB)
-constexpr int kPerThread = 4;   // consecutive positions per thread in the ordered pass
+constexpr int kPerThread = 16;  // consecutive positions per thread in the ordered pass (kKeyCap / kSelThreads)
+constexpr int kMaxBins = 4096;  // the widest digit: 12 bits
 
 // f32 -> u32 with the same order (larger value, larger key); -inf is the
 // smallest non-NaN key, and a masked position takes that key.
@@ -33,9 +35,10 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 }
 constexpr uint32_t kKeyNegInf = 0x007fffffu;  // order_key(-inf)
 
-// Exclusive prefix sum over the workgroup of v (each thread's value); the total
-// goes to *total.  Uses sums[4] in LDS; all threads call it.
-__device__ __forceinline__ uint32_t wg_exclusive_sum(uint32_t v, uint32_t *sums, uint32_t *total) {
+// Inclusive prefix sum over the workgroup of v (each thread's value, in thread
+// order); the total goes to *total.  Uses sums[kSelThreads / 64] in LDS; all
+// threads call it.
+__device__ __forceinline__ uint32_t wg_inclusive_sum(uint32_t v, uint32_t *sums, uint32_t *total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint32_t x = v;
 #pragma unroll
@@ -45,13 +48,16 @@ __device__ __forceinline__ uint32_t wg_exclusive_sum(uint32_t v, uint32_t *sums,
     }
     if (lane == 63) sums[wave] = x;
     __syncthreads();
-    uint32_t before = 0;
+    uint32_t before = 0, all = 0;
 #pragma unroll
-    for (int w = 0; w < kSelThreads / 64; ++w)
-        if (w < wave) before += sums[w];
-    *total = sums[0] + sums[1] + sums[2] + sums[3];
+    for (int w = 0; w < kSelThreads / 64; ++w) {
+        const uint32_t sw = sums[w];
+        before += w < wave ? sw : 0u;
+        all += sw;
+    }
+    *total = all;
     __syncthreads();  // sums may be reused by the next call
-    return before + x - v;
+    return before + x;
 }
 
 template <bool CACHED>
@@ -60,9 +66,11 @@ __global__ void __launch_bounds__(kSelThreads) indexer_topk_kernel(const float *
                                                                    int32_t topk, int32_t offset,
                                                                    int32_t *__restrict__ out, int64_t row_stride,
                                                                    int32_t col0) {
-    __shared__ uint32_t keys[CACHED ? kKeyCap : 1];
-    __shared__ uint32_t hist[256];
-    __shared__ uint32_t sums[4];
+    // key t at word t + t / 16: a thread's 16 consecutive keys (the ordered pass)
+    // then sit in 16 different banks across the lanes of a read
+    __shared__ uint32_t keys[CACHED ? kKeyCap + kKeyCap / 16 : 1];
+    __shared__ uint32_t hist[kMaxBins];
+    __shared__ uint32_t sums[kSelThreads / 64];
     __shared__ uint32_t pick[2];  // digit, count of matching keys above it
 
     const int tid = threadIdx.x;
@@ -72,7 +80,7 @@ __global__ void __launch_bounds__(kSelThreads) indexer_topk_kernel(const float *
     const float *sr = scores + r * T;
     int32_t *orow = out + r * row_stride + col0;
     auto key_of = [&](int t) -> uint32_t {
-        if (CACHED) return keys[t];
+        if (CACHED) return keys[t + (t >> 4)];
         return t < cl ? order_key(sr[t]) : kKeyNegInf;
     };
 
@@ -81,57 +89,72 @@ __global__ void __launch_bounds__(kSelThreads) indexer_topk_kernel(const float *
         return;
     }
     if (CACHED) {
-        for (int t = tid; t < T; t += kSelThreads) keys[t] = t < cl ? order_key(sr[t]) : kKeyNegInf;
+        // every load of the row in flight at once, then the keys into LDS
+        constexpr int KPT = kKeyCap / kSelThreads;
+        float v[KPT];
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int t = tid + i * kSelThreads;
+            v[i] = t < T ? sr[t] : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int t = tid + i * kSelThreads;
+            if (t < T) keys[t + (t >> 4)] = t < cl ? order_key(v[i]) : kKeyNegInf;
+        }
     }
 
-    // ---- radix select of the threshold key: topk-th largest ----
+    // ---- radix select of the threshold key (the topk-th largest): digits of
+    //      12, 10 and 10 bits, most significant first.  The wide first digit
+    //      (sign, exponent, 3 mantissa bits) spreads scores that share a few
+    //      binades over many bins, so the histogram atomics rarely collide; the
+    //      later digits only count the few keys still matching. ----
     uint32_t prefix = 0, pmask = 0;
     uint32_t need = (uint32_t)topk;  // how many keys matching the prefix are still to take
 #pragma unroll 1
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        hist[tid] = 0;  // (kSelThreads == 256 bins)
+    for (int pass = 0; pass < 3; ++pass) {
+        const int width = pass == 0 ? 12 : 10;
+        const int shift = pass == 0 ? 20 : (pass == 1 ? 10 : 0);
+        const int nb = 1 << width;
+        const uint32_t dmask = (uint32_t)nb - 1u;
+        for (int i = tid; i < nb; i += kSelThreads) hist[i] = 0;
         __syncthreads();
+#pragma unroll 16
         for (int t = tid; t < T; t += kSelThreads) {
             const uint32_t k = key_of(t);
-            if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+            if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
         }
         __syncthreads();
-        if (tid < 64) {
-            // lane l holds bins 4 l .. 4 l + 3; suffix sums from the top bin down
-            const uint32_t h0 = hist[4 * tid], h1 = hist[4 * tid + 1], h2 = hist[4 * tid + 2], h3 = hist[4 * tid + 3];
-            const uint32_t c = h0 + h1 + h2 + h3;
-            uint32_t sfx = c;  // sum over lanes >= this one
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const uint32_t y = __shfl_down(sfx, o, 64);
-                if (tid + o < 64) sfx += y;
-            }
-            const uint64_t ok = __ballot(sfx >= need);  // lane 0 always qualifies
-            const int L = 63 - __builtin_clzll(ok);     // highest lane whose suffix reaches need
-            if (tid == L) {
-                uint32_t cum = sfx - c;                 // keys in bins above this lane's
-                const uint32_t hb[4] = {h0, h1, h2, h3};
-                int digit = 4 * L;
-                for (int j = 3; j >= 0; --j) {
-                    if (cum + hb[j] >= need) {
-                        digit = 4 * L + j;
-                        break;
-                    }
-                    cum += hb[j];
+        // thread i holds bins [i * bpt, (i + 1) * bpt); the counts above its bins
+        // come from a prefix sum over the threads (total minus the inclusive sum)
+        const int bpt = nb / kSelThreads;
+        uint32_t c = 0;
+        for (int j = 0; j < bpt; ++j) c += hist[tid * bpt + j];
+        uint32_t total;
+        const uint32_t incl = wg_inclusive_sum(c, sums, &total);
+        uint32_t cum = total - incl;  // keys in the bins above this thread's
+        if (cum < need && cum + c >= need) {  // exactly one thread: the threshold bin is here
+            int digit = tid * bpt;
+            for (int j = bpt - 1; j >= 0; --j) {
+                const uint32_t h = hist[tid * bpt + j];
+                if (cum + h >= need) {
+                    digit = tid * bpt + j;
+                    break;
                 }
-                pick[0] = (uint32_t)digit;
-                pick[1] = cum;
+                cum += h;
             }
+            pick[0] = (uint32_t)digit;
+            pick[1] = cum;
         }
         __syncthreads();
         prefix |= pick[0] << shift;
-        pmask |= 255u << shift;
+        pmask |= dmask << shift;
         need -= pick[1];
         __syncthreads();  // pick and hist are rewritten by the next pass
     }
     const uint32_t thr = prefix;  // keys above are all taken, `need` of those equal to it
 
-    // ---- ordered pass: positions in order, 4 consecutive per thread ----
+    // ---- ordered pass: positions in order, kPerThread consecutive per thread ----
     uint32_t written = 0, eq_left = need;
     for (int base = 0; base < T; base += kSelThreads * kPerThread) {
         const int t0 = base + kPerThread * tid;
@@ -143,9 +166,9 @@ __global__ void __launch_bounds__(kSelThreads) indexer_topk_kernel(const float *
             n_gt += (t0 + j < T && kk[j] > thr) ? 1u : 0u;
             n_eq += (t0 + j < T && kk[j] == thr) ? 1u : 0u;
         }
-        // (at most kSelThreads * kPerThread = 1024 per tile: two 16-bit counts in one word)
+        // (at most kSelThreads * kPerThread = 16384 per tile: two 16-bit counts in one word)
         uint32_t tot;
-        const uint32_t pre = wg_exclusive_sum(n_gt | (n_eq << 16), sums, &tot);
+        const uint32_t pre = wg_inclusive_sum(n_gt | (n_eq << 16), sums, &tot) - (n_gt | (n_eq << 16));
         const uint32_t gt_before = pre & 0xffffu, eq_before = pre >> 16;
         // equal keys are taken in position order while their rank among the equal
         // keys still to take is below eq_left

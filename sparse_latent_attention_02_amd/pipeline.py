@@ -28,12 +28,17 @@ import torch
 from . import sparse_attn, window_kv_update, window_topk_idxs, append_compressed_idxs, act_quant_fp8_
 from . import workspace_bytes, sparse_attn_decode_step, decode_step_workspace_bytes
 from . import kv8_pack, kv8_workspace_bytes, sparse_attn_decode_step_kv8
-from .workloads import WORKLOADS
+from .workloads import WORKLOADS, rope_table
+
+ROPE_DIM = 64  # the rotated part of each latent row (the model's rope head dim)
 
 
-def prepare(wid: int, raw: dict, device: str = "cuda", kv8: bool = False) -> SimpleNamespace:
+def prepare(wid: int, raw: dict, device: str = "cuda", kv8: bool = False, rope_dim: int = 0) -> SimpleNamespace:
     w = WORKLOADS[wid]
-    st = SimpleNamespace(w=w, wid=wid, kv8=kv8)
+    st = SimpleNamespace(w=w, wid=wid, kv8=kv8, rope=None)
+    if rope_dim:
+        # one table row per position the step's queries sit at
+        st.rope = (rope_table(2000 + wid, w.start_pos + w.s, rope_dim).to(device), rope_dim)
     if kv8 and w.start_pos == 0:
         raise ValueError("the fp8-resident cache is read by the decode step only")
     st.sink = raw["sink"].to(device)
@@ -91,7 +96,8 @@ def update_and_index(st: SimpleNamespace) -> None:
 def attend(st: SimpleNamespace) -> torch.Tensor:
     """Step 4."""
     w = st.w
-    return sparse_attn(st.q, st.kv, st.sink, st.idx, w.scale, out=st.out, workspace=st.ws)
+    rope = (st.rope[0], st.rope[1], w.start_pos) if st.rope else None
+    return sparse_attn(st.q, st.kv, st.sink, st.idx, w.scale, out=st.out, workspace=st.ws, rope=rope)
 
 
 def step(st: SimpleNamespace) -> torch.Tensor:
@@ -127,7 +133,7 @@ def step_fused(st: SimpleNamespace) -> torch.Tensor:
     assert w.start_pos > 0, "the fused step is a decode step"
     return sparse_attn_decode_step(st.q, st.kv, st.new_rows.view(w.b, w.d), st.sink, w.window, w.start_pos,
                                    w.scale, cidx=st.comp.view(w.b, w.n_comp) if st.comp is not None else None,
-                                   out=st.out, idx_out=st.idx, workspace=st.ws)
+                                   out=st.out, idx_out=st.idx, workspace=st.ws, rope=st.rope)
 
 
 def step_fused_kv8(st: SimpleNamespace) -> torch.Tensor:

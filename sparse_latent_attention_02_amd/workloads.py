@@ -161,3 +161,16 @@ def rope_table(seed: int, n_pos: int, rope_dim: int) -> torch.Tensor:
     g = torch.Generator().manual_seed(seed)
     th = (torch.rand((n_pos, rope_dim // 2), generator=g, dtype=torch.float64) * 2 - 1) * torch.pi
     return torch.stack([torch.cos(th), torch.sin(th)], dim=-1).to(torch.float32).contiguous()
+
+
+# The indexer selection tail's workload: the compressed half of the decode +
+# compressed configuration -- 128 single-query sequences whose indexer scores
+# 16384 compressed positions (start_pos 65535, ratio 4) and keeps 2048 of them,
+# placed after the 128 window columns.  Scores are N(0, 1) f32 (the pages'
+# scores come from trained weights).
+SELECT_WORKLOAD = dict(b=128, s=1, start_pos=65535, ratio=4, index_topk=2048, offset=128)
+
+
+def indexer_scores(seed: int, b: int, s: int, n_cols: int) -> torch.Tensor:
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn((b, s, n_cols), generator=g, dtype=torch.float32)
