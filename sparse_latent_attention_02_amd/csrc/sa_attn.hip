@@ -124,6 +124,20 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const SA_LDS char *p) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Wait until at most n (wave-uniform, 0..16) vector-memory operations of this
+// wave are outstanding; the count is an immediate of the instruction, so the
+// value selects one of the fixed waits.
+__device__ __forceinline__ void wait_vmcnt_upto16(int n) {
+#define SA_VMW(k) \
+    case k: asm volatile("s_waitcnt vmcnt(" #k ")" : : : "memory"); break;
+    switch (__builtin_amdgcn_readfirstlane(n)) {
+        SA_VMW(1) SA_VMW(2) SA_VMW(3) SA_VMW(4) SA_VMW(5) SA_VMW(6) SA_VMW(7) SA_VMW(8)
+        SA_VMW(9) SA_VMW(10) SA_VMW(11) SA_VMW(12) SA_VMW(13) SA_VMW(14) SA_VMW(15) SA_VMW(16)
+        default: asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); break;
+    }
+#undef SA_VMW
+}
+
 // Copy of query qi's rotation table row (rope_dim floats, in 16-byte chunks,
 // up to two wave instructions) into LDS at tab; called by one whole wavefront.
 __device__ __forceinline__ void copy_rope_row(const AttnParams &p, uint32_t qi, int lane, uint32_t tab) {
@@ -821,6 +835,7 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
     uint32_t okm_cur = 0, okm_nxt = 0;
     uint64_t src_nxt = 0;
     int rowv_nxt = 0;
+    int n_early = 0;  // bf16 rows: stage 1's copies, issued in the prologue
     if (nst > 0) {
         store_idx(0, v0);
         // the output rotation's table row for this query (the first stage's wait covers it)
@@ -849,6 +864,17 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
             prep(0, v0, okm_cur, src0);
 #pragma unroll 1
             for (int u = 0; u < C::RPW; ++u) copy_rows(0, okm_cur, src0, u, u + 1);
+            if (nst > 1) {
+                // stage 1 goes out right behind stage 0 (its buffer is free): the
+                // copies are all in flight before any compute, and stage 0's score
+                // product runs without copy issue in between
+                store_idx(1, v_up);
+                prep(1, v_up, okm_nxt, src_nxt);
+#pragma unroll 1
+                for (int u = 0; u < C::RPW; ++u) copy_rows(1, okm_nxt, src_nxt, u, u + 1);
+                n_early = __builtin_popcount(okm_nxt);  // stage 1's copies (rows of -1 are zero-filled instead)
+                v_up = v_after;                          // entries of stage 2 (stage 3's are fetched later)
+            }
         }
     }
 
@@ -864,8 +890,12 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
     for (int t = 0; t < nst; ++t) {
         const int ebase = lo + t * C::ROWS;
         const SA_LDS char *stage = lds + (KV8 ? 0 : (t & 1) * C::STAGE_BYTES);
-        // ---- this wave's copies of stage t complete ----
-        asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+        // ---- this wave's copies of stage t complete (at stage 0 of the bf16 rows,
+        //      stage 1's copies behind them may still fly) ----
+        if (!KV8 && t == 0 && nst > 1)
+            wait_vmcnt_upto16(n_early);
+        else
+            asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
         if (KV8 && t == 0) asm volatile("" : : "v"(new_raw));  // (it was loaded before any copy)
         if (!KV8 && FUSED && t == st_new && wave == w_new) {
             // the raw new row has landed: round it through fp8 in place
@@ -908,7 +938,8 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
             lds_barrier();
         }
         const bool more = t + 1 < nst;  // stage t+1 goes into the buffer stage t-1 used
-        if (more) {
+        const bool issue = more && (KV8 || t > 0);  // (bf16 rows: stage 1 went out in the prologue)
+        if (issue) {
             store_idx(t + 1, v_up);
             if constexpr (KV8)
                 prep8(v_up, okm_nxt, rowv_nxt);
@@ -929,7 +960,7 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
         for (int ks = 0; ks < C::KS; ks += 2) {
             const bf16x8_t a0 = lds_read_b128(kb + 64 * ks);
             const bf16x8_t a1 = lds_read_b128(kb + 64 * (ks + 1));
-            if (more) {
+            if (issue) {
                 if constexpr (KV8)
                     copy8(t + 1, okm_nxt, rowv_nxt, (ks / 2) * (C::NCI8 + 1) / (C::KS / 2),
                           (ks / 2 + 1) * (C::NCI8 + 1) / (C::KS / 2));
@@ -940,7 +971,7 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
             s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qreg[ks + 1], s1, 0, 0, 0);
         }
         if (more) {
-            v_up = v_after;
+            if (issue) v_up = v_after;  // (bf16 rows: shifted in the prologue for stage 0)
             v_after = fetch_stage(t + 3);
         }
         // value i of lane (g, n): row RPW wave + 4 g + i, head n
@@ -966,20 +997,27 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
             }
             m_ref = m_new;
         }
-        // weights -> bf16 -> P[head][row] in LDS (rows RPW wave + 4 g + 0..3)
+        // weights -> bf16 -> P[head][k] in LDS.  Within each block of 8 rows the
+        // contraction index k takes the even rows first, then the odd ones (k = 2 j
+        // <-> row 2 j, k = 4 + j <-> row 2 j + 1), the order the V reads below use;
+        // this lane's rows RPW wave + 4 g + i sit at k positions (i0, i2) and
+        // (i1, i3) of its block half.
         {
-            const uint32_t b0 = pack_bf16x2(exp2_fast(sv[0] - m_ref), exp2_fast(sv[1] - m_ref));
-            const uint32_t b1 = pack_bf16x2(exp2_fast(sv[2] - m_ref), exp2_fast(sv[3] - m_ref));
-            l_run += __uint_as_float(b0 << 16) + __uint_as_float(b0 & 0xffff0000u) + __uint_as_float(b1 << 16) +
-                     __uint_as_float(b1 & 0xffff0000u);
-            *reinterpret_cast<SA_LDS u32x2_t *>((SA_LDS char *)pbuf + n * C::PRS + 2 * (C::RPW * wave + 4 * g)) =
-                u32x2_t{b0, b1};
+            const uint32_t wa = pack_bf16x2(exp2_fast(sv[0] - m_ref), exp2_fast(sv[2] - m_ref));
+            const uint32_t wb = pack_bf16x2(exp2_fast(sv[1] - m_ref), exp2_fast(sv[3] - m_ref));
+            l_run += __uint_as_float(wa << 16) + __uint_as_float(wb << 16) + __uint_as_float(wa & 0xffff0000u) +
+                     __uint_as_float(wb & 0xffff0000u);
+            SA_LDS char *pw = (SA_LDS char *)pbuf + n * C::PRS + 2 * (C::RPW * wave + 8 * (g >> 1) + 2 * (g & 1));
+            *reinterpret_cast<SA_LDS uint32_t *>(pw) = wa;
+            *reinterpret_cast<SA_LDS uint32_t *>(pw + 8) = wb;
         }
         lds_barrier();
 
         // ---- O^T[this wave's d quarter][16 heads] += V^T P^T over the stage's rows ----
-        // (transposing read: rows 32 ks + 8 g + 4 rd + p/4, d 16 dt + 4 (p%4) of the quarter)
-        const SA_LDS char *vb = stage + (8 * g + (n >> 2)) * C::RS + 2 * C::DQ * wave + 8 * (n & 3);
+        // (transposing read: the 16 lanes of group g read rows 32 ks + 8 g + 2 (n / 4)
+        // (+1 for the upper half of k), d 16 dt + 4 (n % 4) of the quarter; rows two
+        // apart put the four 32-byte row pieces of one read on disjoint banks)
+        const SA_LDS char *vb = stage + (8 * g + 2 * (n >> 2)) * C::RS + 2 * C::DQ * wave + 8 * (n & 3);
 #pragma unroll
         for (int ks = 0; ks < C::ROWS / 32; ++ks) {
             if (32 * ks < hi - ebase) {  // k-steps past the list end hold only zero weights
@@ -990,7 +1028,7 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
 #pragma unroll
                 for (int dt = 0; dt < C::DT; ++dt) {
                     lo4[dt] = lds_read_tr16(vb + (32 * ks) * C::RS + 32 * dt);
-                    hi4[dt] = lds_read_tr16(vb + (32 * ks + 4) * C::RS + 32 * dt);
+                    hi4[dt] = lds_read_tr16(vb + (32 * ks + 1) * C::RS + 32 * dt);
                 }
 #pragma unroll
                 for (int dt = 0; dt < C::DT; ++dt) {
