@@ -83,19 +83,21 @@ struct AttnParams {
     int32_t kc;              // compressed columns
     int32_t wbase;           // (pos + 1) % window: slot of the oldest entry
     int32_t new_slot;        // pos % window: slot of the new row (list entry window - 1)
-    // fp8-resident rows (kv8): e4m3fn codes [..][rows][d] and 16-byte scale
-    // records [..][rows][16] in place of kv; the fused step writes the new
-    // row's codes and scale record into its ring slot
-    const uint8_t *kv8c;
-    const uint8_t *kv8s;
-    uint8_t *kv8c_ring;
-    uint8_t *kv8s_ring;
     // inverse rotation of the output's last rope_dim values (null rope: none):
     // query (b, s) at position rope_pos0 + s, table [positions][rope_dim / 2] of
     // (cos, sin) f32
     const float *rope;
     int32_t rope_dim;
     int64_t rope_pos0;
+    // fp8-resident rows (kv8): e4m3fn codes [..][rows][d] and 16-byte scale
+    // records [..][rows][16] in place of kv; the fused step writes the new
+    // row's codes and scale record into its ring slot.  (Last: the bf16 kernels
+    // never read them, so their arguments stay within three 64-byte lines,
+    // all loaded at kernel start.)
+    const uint8_t *kv8c;
+    const uint8_t *kv8s;
+    uint8_t *kv8c_ring;
+    uint8_t *kv8s_ring;
 };
 
 // Entry e of a decode step's concatenated list: the ring listed oldest first,
@@ -711,24 +713,53 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
     const int hi = min(p.topk, lo + p.split_len);
     const int nst = hi > lo ? (hi - lo + C::ROWS - 1) / C::ROWS : 0;
     const int32_t *idxq = FUSED ? nullptr : p.idx + (int64_t)qi * p.topk;
-    auto fetch = [&](int e) -> int { return FUSED ? step_entry(p, qi, e) : idxq[e]; };
 
     // this wave's 16 entries of a stage sit in lanes 0..15 (mirrored in the other
     // lane groups); the first three stages' go in flight before anything else
     const int head = (int)hg * C::HEADS + n;
     const bool head_ok = head < p.h;
     // the head's sink, loaded before any copy goes out (a load issued after them
-    // would wait behind them at the end)
-    const float sink_h = (head_ok && p.n_sp == 1) ? p.sink[head] : 0.0f;
+    // would wait behind them at the end).  Without the ring formula, every load
+    // here is unconditional, from a clamped address, with the value masked
+    // afterwards: a load inside a divergent branch gets a wait for it at the
+    // branch's end, which would put a memory latency on the startup path.  (The
+    // one-launch step keeps the conditional forms: measured faster there.)
+    float sink_h;
+    if (FUSED) {
+        sink_h = (head_ok && p.n_sp == 1) ? p.sink[head] : 0.0f;
+    } else {
+        const float sink_any = p.sink[min(head, p.h - 1)];
+        sink_h = (head_ok && p.n_sp == 1) ? sink_any : 0.0f;
+    }
     const bool rot = p.rope != nullptr && p.n_sp == 1 && nst > 0;
     const int eoff = C::RPW * wave + (lane & 15);
+    // (a readable dummy for a load whose value is not needed: the sink)
+    const int32_t *dummy = reinterpret_cast<const int32_t *>(p.sink);
     auto fetch_stage = [&](int j) -> int {
         const int e = lo + j * C::ROWS + eoff;
-        return e < hi ? fetch(e) : -1;
+        if (FUSED) return e < hi ? step_entry(p, qi, e) : -1;
+        const int v = *(hi > lo ? idxq + min(e, hi - 1) : dummy);
+        return e < hi ? v : -1;
     };
-    const int v0 = fetch_stage(0);
-    int v_up = fetch_stage(1);     // entries of the next stage to copy
-    int v_after = fetch_stage(2);  // and of the one after
+    // The first three stages' entries.  Index lists: the loads go out together
+    // inside one uniform branch, so one memory latency covers them.
+    int v0, v_up, v_after;  // entries of stages 0, 1 (the next to copy), 2
+    if (FUSED) {
+        v0 = fetch_stage(0);
+        v_up = fetch_stage(1);
+        v_after = fetch_stage(2);
+    } else {
+        const int e0 = lo + eoff, e1 = e0 + C::ROWS, e2 = e0 + 2 * C::ROWS;
+        int a0 = -1, a1 = -1, a2 = -1;
+        if (hi > lo) {
+            a0 = idxq[min(e0, hi - 1)];
+            a1 = idxq[min(e1, hi - 1)];
+            a2 = idxq[min(e2, hi - 1)];
+        }
+        v0 = e0 < hi ? a0 : -1;
+        v_up = e1 < hi ? a1 : -1;
+        v_after = e2 < hi ? a2 : -1;
+    }
     // the entries are in registers before any copy goes out: a compiler-placed wait
     // for them after the copies would also wait for the copies
     asm volatile("" : : "v"(v0), "v"(v_up), "v"(v_after));
