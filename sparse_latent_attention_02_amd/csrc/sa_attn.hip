@@ -165,13 +165,31 @@ __device__ __forceinline__ u32x4_t unrotate_chunk(u32x4_t v, int d0, int d, int 
     return v;
 }
 
-// Logical workgroup id.  The dispatcher hands workgroups to the 8 XCDs round
-// robin; the remap gives each XCD a contiguous range of logical ids, so rows
-// shared by neighbouring queries (prefill windows) or by the head groups and
-// splits of one query stay in that XCD's L2.
+// Logical workgroup id (decode kernel).  The dispatcher hands workgroups to the
+// 8 XCDs round robin; the remap gives each XCD a contiguous range of logical
+// ids, so the head groups and splits of one query, which gather the same rows,
+// share that XCD's L2.
 __device__ __forceinline__ uint32_t logical_wg(uint32_t T) {
     const uint32_t per = T >> 3, rem = T & 7, x = blockIdx.x & 7, k = blockIdx.x >> 3;
     return x < rem ? x * (per + 1) + k : rem * (per + 1) + (x - rem) * per + k;
+}
+
+// Wide-kernel workgroup -> (query, j = head group * n_sp + split); false for a
+// padding workgroup.  The dispatcher hands block b to XCD b % 8, each XCD taking
+// its blocks in order.  A query's n_hg * n_sp workgroups are consecutive blocks
+// of one XCD (they gather the same rows: the later ones hit that XCD's L2);
+// queries are dealt to the XCDs in turn, so lists whose length grows with the
+// query position (a causal prefill) load every XCD alike; and the highest query
+// index goes first (the longest list of a causal prefill: long work first leaves
+// short work for the tail).  The grid holds 8 * ceil(nq / 8) queries' worth of
+// workgroups.
+__device__ __forceinline__ bool wide_unit(const AttnParams &p, uint32_t &qi, uint32_t &j) {
+    const uint32_t g = (uint32_t)(p.n_hg * p.n_sp);
+    const uint32_t k = blockIdx.x >> 3, m = k / g;
+    j = k - m * g;
+    const uint32_t rounds = ((uint32_t)p.nq + 7u) >> 3;
+    qi = 8u * (rounds - 1u - m) + (blockIdx.x & 7u);
+    return qi < (uint32_t)p.nq;
 }
 
 // Index-list compaction.  The entries of idx[c0, c1) (at most kListCap) are
@@ -307,11 +325,10 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
     const int rh = wave & 1;   // row half of every stage this wavefront computes
     const bool chunk_lane = C::CH == 64 || lane < C::CH;
 
-    const uint32_t L = logical_wg((uint32_t)p.total_wg);
-    const uint32_t sp = L % (uint32_t)p.n_sp;
-    const uint32_t t2 = L / (uint32_t)p.n_sp;
-    const uint32_t hg = t2 % (uint32_t)p.n_hg;
-    const uint32_t qi = t2 / (uint32_t)p.n_hg;
+    uint32_t qi, j;
+    if (!wide_unit(p, qi, j)) return;  // (uniform over the workgroup, before any barrier)
+    const uint32_t sp = j % (uint32_t)p.n_sp;
+    const uint32_t hg = j / (uint32_t)p.n_sp;
     const uint32_t bi = qi / (uint32_t)p.s;
 
     const int lo = (int)sp * p.split_len;
@@ -1330,7 +1347,9 @@ AttnParams base_params(const uint16_t *q, const uint16_t *kv, const float *sink,
 
 template <bool FUSED, bool KV8>
 sa_status enqueue(AttnParams &p, const Variant &v, int32_t d, hipStream_t hs) {
-    const int64_t total = (int64_t)p.nq * p.n_hg * v.n_sp;
+    // decode kernel: one block per workgroup; wide kernel: 8 * ceil(nq / 8) queries' worth
+    const int64_t units = v.kernel == SA_KERNEL_DECODE ? (int64_t)p.nq : 8 * (((int64_t)p.nq + 7) / 8);
+    const int64_t total = units * p.n_hg * v.n_sp;
     if (total > 0x7fffffffLL) return SA_ERR_SHAPE;
     p.total_wg = (int32_t)total;
     if (launch_attn<FUSED, KV8>(p, v, d, hs) != hipSuccess) return SA_ERR_HIP;
