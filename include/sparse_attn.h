@@ -210,7 +210,12 @@ typedef enum {
     /* one workgroup of four wavefronts per (query, 16 heads); 64-row stages,
      * two buffers deep, whose rows the wavefronts split for the scores and
      * whose head dim they split for the weighted sum (decode-sized batches) */
-    SA_KERNEL_DECODE = 2
+    SA_KERNEL_DECODE = 2,
+    /* one workgroup of two wavefronts per (query, 64 heads); each wavefront
+     * holds 32 heads over the whole head dim and walks every row of the list in
+     * 32-row stages (no merge between wavefronts); under 80 KiB of LDS, so two
+     * workgroups share a CU (grids of many workgroups: prefill) */
+    SA_KERNEL_PAIR = 3
 } sa_kernel;
 
 /* Same operation with the variant forced (for tests and measurement):

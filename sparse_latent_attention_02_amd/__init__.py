@@ -30,7 +30,7 @@ LIB_PATH = os.path.join(_HERE, "libsparse_attn.so")
 _lib = None
 
 SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_UNSUPPORTED, SA_ERR_HIP = 0, 1, 2, 3, 4
-SA_KERNEL_AUTO, SA_KERNEL_WIDE, SA_KERNEL_DECODE = 0, 1, 2
+SA_KERNEL_AUTO, SA_KERNEL_WIDE, SA_KERNEL_DECODE, SA_KERNEL_PAIR = 0, 1, 2, 3
 KV8_SCALE_BYTES = 16
 
 

@@ -192,14 +192,14 @@ __device__ __forceinline__ bool wide_unit(const AttnParams &p, uint32_t &qi, uin
     return qi < (uint32_t)p.nq;
 }
 
-// Index-list compaction.  The entries of idx[c0, c1) (at most kListCap) are
+// Index-list compaction.  The entries of idx[c0, c1) (at most CAP) are
 // spread over the workgroup's threads as e = c0 + k * NT + tid, k < K, and all
 // K loads of a thread are issued together, so a chunk costs one memory latency.
 // Valid entries (0 <= v < rows) are packed into list[0, nv) in (k, thread)
 // order -- deterministic, and any order is correct (each entry is independent).
-template <int NT>
+template <int NT, int CAP = kListCap>
 struct Compactor {
-    static constexpr int K = kListCap / NT;
+    static constexpr int K = CAP / NT;
     static constexpr int NW = NT / 64;
     int v[K];
 
@@ -648,6 +648,299 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
     }
     lds_barrier();
     // one head row per wave instruction: lane l stores chunk l (16 B) of the row
+#pragma unroll 4
+    for (int hr = wave; hr < C::HEADS; hr += C::NW) {
+        const int hglob = (int)hg * C::HEADS + hr;
+        if (hglob < p.h && chunk_lane) {
+            u32x4_t v = *reinterpret_cast<const SA_LDS u32x4_t *>(stg + hr * C::RS + 16 * lane);
+            if (rot) v = unrotate_chunk(v, 8 * lane, D, p.rope_dim, (const SA_LDS float *)rtab);
+            *reinterpret_cast<u32x4_t *>(p.out + ((int64_t)qi * p.h + hglob) * D + lane * 8) = v;
+        }
+    }
+}
+
+// ------------------------------------------------------------------- pair --
+//
+// Pair kernel: one workgroup of two wavefronts per (query, 64 heads[, index
+// split]), for grids of many workgroups (prefill).  Each wavefront owns a
+// 32-head tile over the whole head dim (Q in registers, loaded straight from
+// memory: no other wavefront needs it; O in accumulator registers) and walks
+// every row of the list in 32-row stages: S^T[32 rows][32 heads] = K Q^T, the
+// softmax against the fixed reference of the wide kernel, O^T[d][32 heads] +=
+// V^T P^T, all on MFMA 32x32x16 with the operand layouts of the wide kernel.
+// A wavefront thus ends with its heads' whole result: no merge between
+// wavefronts.  With 32-row stages and a 2048-entry list chunk the workgroup
+// needs under 80 KiB of LDS, so two workgroups share a CU and the prologue
+// (list compaction, Q loads) and epilogue (normalisation, stores) of one
+// overlap the stages of the other.
+template <int D>
+struct PairCfg {
+    static constexpr int NW = 2;
+    static constexpr int THREADS = 64 * NW;
+    static constexpr int HEADS = 64;
+    static constexpr int ROWS = 32;             // rows per stage (all of them, for each wavefront)
+    static constexpr int RPW = ROWS / NW;       // rows each wavefront copies per stage
+    static constexpr int RS = 2 * D + 48;       // LDS row stride, as in the wide kernel
+    static constexpr int CH = D / 8;
+    static constexpr int KS = D / 16;
+    static constexpr int DT = D / 32;
+    static constexpr int STAGE_BYTES = ROWS * RS;
+    static constexpr int NBUF = 2;
+    static constexpr int LIST_CAP = 2048;       // compacted entries held at once
+    static constexpr int OUT_BYTES = HEADS * RS;  // staged bf16 output, over the stage buffers
+    static constexpr int SMEM = std::max(NBUF * STAGE_BYTES, OUT_BYTES);
+    static constexpr float SLACK = 32.0f;
+    static constexpr int PFK = D > 256 ? 2 : 4;
+    static constexpr int PFV = D > 256 ? 2 : 3;
+    static constexpr int copy_at(int i) { return (i * RPW + KS - 1) / KS; }
+    static_assert(KS >= 4 && DT >= 2 && RPW == 16, "tiling");
+};
+
+template <int D, bool FUSED>
+__global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const AttnParams p) {
+    using C = PairCfg<D>;
+    __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
+    __shared__ int list[C::LIST_CAP];
+    __shared__ int wcnt[C::LIST_CAP / 64];
+    __shared__ int replay[2];
+    __shared__ __attribute__((aligned(16))) float rtab[D];  // the query's rotation table row
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // head tile
+    const int lane = tid & 63;
+    const int hf = lane >> 5;
+    const int n = lane & 31;
+    const bool chunk_lane = C::CH == 64 || lane < C::CH;
+
+    uint32_t qi, j;
+    if (!wide_unit(p, qi, j)) return;  // (uniform over the workgroup, before any barrier)
+    const uint32_t sp = j % (uint32_t)p.n_sp;
+    const uint32_t hg = j / (uint32_t)p.n_sp;
+    const uint32_t bi = qi / (uint32_t)p.s;
+
+    const int lo = (int)sp * p.split_len;
+    const int hi = min(p.topk, lo + p.split_len);
+    const int32_t *idxq = FUSED ? nullptr : p.idx + (int64_t)qi * p.topk;
+    auto fetch = [&](int e) -> int { return FUSED ? step_entry(p, qi, e) : idxq[e]; };
+    const bool has_new = FUSED && p.window - 1 >= lo && p.window - 1 < hi;
+    u32x4_t new_raw = {0u, 0u, 0u, 0u};
+    if (has_new && wave == 0 && chunk_lane)
+        new_raw = *reinterpret_cast<const u32x4_t *>(p.kv_new + (int64_t)qi * D + lane * 8);
+    // the first index chunk goes in flight before anything else: it heads the critical path
+    Compactor<C::THREADS, C::LIST_CAP> cmp;
+    cmp.load(fetch, lo, min(hi, lo + C::LIST_CAP));
+
+    // Q as the B operand, straight from memory: lane (hf, n) holds
+    // q[head n][16 ks + 8 hf .. +8] for every ks (zeros past h)
+    const int head = ((int)hg * 2 + wave) * 32 + n;
+    const bool head_ok = head < p.h;
+    bf16x8_t qreg[C::KS];
+    {
+        const uint16_t *qrow = p.q + ((int64_t)qi * p.h + (head_ok ? head : 0)) * D + 8 * hf;
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(qrow + 16 * ks);
+            qreg[ks] = __builtin_bit_cast(bf16x8_t, head_ok ? v : u32x4_t{0u, 0u, 0u, 0u});
+        }
+    }
+
+    cmp.ready();
+    if (has_new && wave == 0) {
+        // the new row rounded through fp8 into its ring slot (as in the wide kernel)
+        const u32x4_t r = fp8_round_trip_chunk(new_raw);
+        if (chunk_lane)
+            *reinterpret_cast<u32x4_t *>(p.kv_ring + ((int64_t)bi * p.rows + p.new_slot) * D + lane * 8) = r;
+        asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+    }
+
+    const uint32_t smem_base = lds_addr((const SA_LDS void *)smem);
+    const bool rot = p.rope != nullptr && p.n_sp == 1;
+    if (rot && wave == 0) copy_rope_row(p, qi, lane, lds_addr((const SA_LDS void *)rtab));
+    const SA_LDS char *lds = (const SA_LDS char *)smem;
+
+    float m_ref = -1e30f;
+    float m_seen = -1e30f;
+    float l_run = 0.0f;
+    f32x16_t acc_o[C::DT];
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) acc_o[dt] = f32x16_t{};
+    if (tid == 0) replay[0] = replay[1] = 0;  // read only after the barriers of pack
+
+    const uint16_t *kvb = p.kv + (int64_t)bi * p.rows * D;
+    const int koff = n * C::RS + 16 * hf;
+    const int p16 = lane & 15;
+    const int voff = (4 * hf + (p16 >> 2)) * C::RS + 16 * (2 * ((lane >> 4) & 1) + ((p16 & 3) >> 1)) +
+                     ((p16 & 1) << 3);
+
+    // weights against a fixed reference max, with a whole-list replay should a
+    // stage max outrun it by more than SLACK (see the wide kernel)
+    bool first_pass = true;
+    for (bool again = true; again; first_pass = false) {
+    again = false;
+    for (int c0 = lo; c0 < hi; c0 += C::LIST_CAP) {
+        const int c1 = min(hi, c0 + C::LIST_CAP);
+        if (c0 != lo || !first_pass) cmp.load(fetch, c0, c1);
+        if (FUSED && first_pass && hg == 0 && p.idx_out) cmp.store(p.idx_out + (int64_t)qi * p.topk, c0, c1);
+        const int nv = cmp.pack(p.rows, list, wcnt);
+        const int nst = (nv + C::ROWS - 1) / C::ROWS;
+        if (nv == 0) continue;
+
+        // copies of stage st into buffer st % 2: this wave's RPW rows, one wave
+        // instruction each; lane u (< RPW) holds the row of copy u, entries past
+        // the list end repeat its last row
+        auto stage_rows = [&](int st) -> int {
+            const int e = st * C::ROWS + wave * C::RPW + (lane & 15);
+            return list[e < nv ? e : nv - 1];
+        };
+        auto copy_rows = [&](int st, int rows_reg, int u0, int u1) {
+            const uint32_t buf = smem_base + (uint32_t)((st & 1) * C::STAGE_BYTES + wave * C::RPW * C::RS);
+            for (int u = u0; u < u1; ++u) {
+                const int row = __builtin_amdgcn_readlane(rows_reg, u);
+                if (chunk_lane) dma_16B(kvb + (int64_t)row * D + lane * 8, buf + u * C::RS);
+            }
+        };
+        {
+            const int r0 = stage_rows(0);
+#pragma unroll 1
+            for (int u = 0; u < C::RPW; ++u) copy_rows(0, r0, u, u + 1);
+        }
+
+        for (int st = 0; st < nst; ++st) {
+            asm volatile("s_waitcnt vmcnt(0)" : : : "memory");  // this wave's copies of stage st
+            lds_barrier();  // both waves' copies in place; stage st-1 consumed, its buffer free
+            if (st > 0 && replay[(st - 1) & 1]) break;          // (no copy in flight here)
+            const SA_LDS char *buf = lds + (st & 1) * C::STAGE_BYTES;
+            const bool more = st + 1 < nst;
+            const int rows_next = more ? stage_rows(st + 1) : 0;
+
+            // ---- scores S^T[32 rows][32 heads]; the next stage's copies spread over them ----
+            f32x16_t sacc = {};
+            {
+                const SA_LDS char *kb = buf + koff;
+                constexpr int PF = C::PFK;
+                bf16x8_t kq[PF];
+#pragma unroll
+                for (int i = 0; i < PF; ++i) kq[i] = lds_read_b128(kb + 32 * i);
+#pragma unroll
+                for (int ks = 0; ks < C::KS; ++ks) {
+                    const bf16x8_t a = kq[ks % PF];
+                    if (ks + PF < C::KS) kq[ks % PF] = lds_read_b128(kb + 32 * (ks + PF));
+                    if (more) copy_rows(st + 1, rows_next, C::copy_at(ks), C::copy_at(ks + 1));
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc, 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+
+            // ---- softmax: value i of lane (hf, n) is row 8(i/4) + 4 hf + i%4, head n ----
+            const int ebase = st * C::ROWS;
+            f32x16_t &sv = sacc;
+            float mx = -INFINITY;
+            if (ebase + 32 <= nv) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    sv[i] = sacc[i] * p.scale_log2;
+                    mx = fmaxf(mx, sv[i]);
+                }
+            } else {  // last, partial stage: rows past the list end weigh nothing
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int r = 8 * (i >> 2) + 4 * hf + (i & 3);
+                    sv[i] = ebase + r < nv ? sacc[i] * p.scale_log2 : -INFINITY;
+                    mx = fmaxf(mx, sv[i]);
+                }
+            }
+            mx = fmaxf(mx, shfl_xor_f32(mx, 32));
+            m_seen = fmaxf(m_seen, mx);
+            if (__ballot(mx > m_ref + C::SLACK)) {
+                if (__ballot(m_ref > -1e29f) && lane == 0) replay[st & 1] = 1;
+                m_ref = m_seen;
+            }
+            uint32_t pk[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t b = pack_bf16x2(exp2_fast(sv[2 * i] - m_ref), exp2_fast(sv[2 * i + 1] - m_ref));
+                pk[i] = b;
+                l_run += __uint_as_float(b << 16) + __uint_as_float(b & 0xffff0000u);
+            }
+            const bf16x8_t pb0 = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
+            const bf16x8_t pb1 = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[4], pk[5], pk[6], pk[7]});
+
+            // ---- O^T += V^T P^T (operand reads as in the wide kernel) ----
+            {
+                const SA_LDS char *vb = buf + voff;
+                auto vread = [&](int jj) {
+                    const int dt = jj % C::DT, kk = jj / C::DT;
+                    const i16x4_t lo4 = lds_read_tr16(vb + (16 * kk) * C::RS + 64 * dt);
+                    const i16x4_t hi4 = lds_read_tr16(vb + (16 * kk + 8) * C::RS + 64 * dt);
+                    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+                };
+                constexpr int NJ = 2 * C::DT;
+                constexpr int PF = C::PFV;
+                bf16x8_t vq[PF];
+#pragma unroll
+                for (int i = 0; i < PF; ++i) vq[i] = vread(i);
+#pragma unroll
+                for (int jj = 0; jj < NJ; ++jj) {
+                    const bf16x8_t a = vq[jj % PF];
+                    if (jj + PF < NJ) vq[jj % PF] = vread(jj + PF);
+                    acc_o[jj % C::DT] =
+                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, jj >= C::DT ? pb1 : pb0, acc_o[jj % C::DT], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+        lds_barrier();  // the last stage's flag is raised by now
+        if (replay[0] | replay[1]) {
+            again = true;
+            break;
+        }
+    }
+    if (again) {
+        lds_barrier();
+        if (tid == 0) replay[0] = replay[1] = 0;
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) acc_o[dt] = f32x16_t{};
+        l_run = 0.0f;
+    }
+    }
+
+    // ---- sink fold + normalise (or f32 partials), stage bf16 rows, store a row per instruction ----
+    l_run += shfl_xor_f32(l_run, 32);  // the head's sum over all rows
+    asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+    const bool split = p.n_sp > 1;
+    if (split) {
+        if (head_ok) {
+            const int64_t prow = ((int64_t)qi * p.n_sp + sp) * p.h + head;
+#pragma unroll
+            for (int k = 0; k < C::DT; ++k)
+#pragma unroll
+                for (int qd = 0; qd < 4; ++qd)
+                    *reinterpret_cast<f32x4_t *>(p.part_o + prow * D + 32 * k + 8 * qd + 4 * hf) =
+                        f32x4_t{acc_o[k][4 * qd], acc_o[k][4 * qd + 1], acc_o[k][4 * qd + 2], acc_o[k][4 * qd + 3]};
+            if (hf == 0) {
+                p.part_ml[prow * 2] = m_ref;
+                p.part_ml[prow * 2 + 1] = l_run;
+            }
+        }
+        return;
+    }
+    const float sink_l2 = head_ok ? p.sink[head] * kLog2e : 0.f;
+    const float Lt = l_run + exp2_fast(sink_l2 - m_ref);
+    const float inv = Lt > 0.f ? 1.0f / Lt : 0.f;
+    lds_barrier();  // stage buffers free
+    SA_LDS char *stg = (SA_LDS char *)smem;
+#pragma unroll
+    for (int k = 0; k < C::DT; ++k) {
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+            // lane (hf, n) holds head n, d = 32 k + 8 qd + 4 hf + (0..3)
+            const f32x16_t &w = acc_o[k];
+            *reinterpret_cast<SA_LDS u32x2_t *>(stg + (wave * 32 + n) * C::RS + 64 * k + 16 * qd + 8 * hf) =
+                u32x2_t{pack_bf16x2(w[4 * qd] * inv, w[4 * qd + 1] * inv),
+                        pack_bf16x2(w[4 * qd + 2] * inv, w[4 * qd + 3] * inv)};
+        }
+    }
+    lds_barrier();
 #pragma unroll 4
     for (int hr = wave; hr < C::HEADS; hr += C::NW) {
         const int hglob = (int)hg * C::HEADS + hr;
@@ -1202,7 +1495,7 @@ __global__ void __launch_bounds__(256) sa_combine_kernel(const float *__restrict
 // ------------------------------------------------------------------ dispatch --
 
 struct Variant {
-    int kernel;     // SA_KERNEL_WIDE or SA_KERNEL_DECODE
+    int kernel;     // SA_KERNEL_WIDE, SA_KERNEL_DECODE or SA_KERNEL_PAIR
     int heads_wg;   // heads per workgroup
     int n_sp;       // index splits across workgroups
     int split_len;  // entries per split
@@ -1227,10 +1520,13 @@ void set_splits(Variant &v, int32_t topk, int n_sp) {
 // Automatic choice from the problem shape and the CU count (thresholds from
 // measurements on MI355X).  Short lists in decode-sized batches (fewer
 // (query, 64-head group) pairs than two per CU) go to the decode kernel on
-// 16-head groups; everything else to the wide kernel.  The index list is split
-// across workgroups (f32 combine pass) only when the chosen kernel would leave
-// CUs idle and the list is long enough to share.
+// 16-head groups; grids of at least four such pairs per CU to the pair kernel
+// (two workgroups per CU overlap each other's prologue and epilogue); the rest
+// to the wide kernel.  The index list is split across workgroups (f32 combine
+// pass) only when the chosen kernel would leave CUs idle and the list is long
+// enough to share.
 constexpr int kDecodeMaxTopk = 512;
+constexpr int kPairMinPerCu = 4;
 
 Variant choose_variant(int64_t nq, int32_t h, int32_t topk, int cus) {
     Variant v{SA_KERNEL_WIDE, 64, 1, std::max(topk, 1)};
@@ -1238,6 +1534,8 @@ Variant choose_variant(int64_t nq, int32_t h, int32_t topk, int cus) {
     if (wide_wgs < 2LL * cus && topk <= kDecodeMaxTopk) {
         v.kernel = SA_KERNEL_DECODE;
         v.heads_wg = 16;
+    } else if (wide_wgs >= (int64_t)kPairMinPerCu * cus) {
+        v.kernel = SA_KERNEL_PAIR;
     }
     const int64_t wgs = nq * ((h + v.heads_wg - 1) / v.heads_wg);
     const int min_len = v.kernel == SA_KERNEL_DECODE ? 128 : 256;
@@ -1255,11 +1553,12 @@ size_t workspace_for(const Variant &v, int64_t nq, int32_t h, int32_t d) {
 
 sa_status resolve_variant(int64_t nq, int32_t h, int32_t topk, int32_t kernel, int32_t splits, Variant *out) {
     Variant v = choose_variant(nq, h, topk, cu_count());
-    if (kernel != 0 && kernel != SA_KERNEL_WIDE && kernel != SA_KERNEL_DECODE) return SA_ERR_UNSUPPORTED;
+    if (kernel != 0 && kernel != SA_KERNEL_WIDE && kernel != SA_KERNEL_DECODE && kernel != SA_KERNEL_PAIR)
+        return SA_ERR_UNSUPPORTED;
     if (splits < 0) return SA_ERR_UNSUPPORTED;
     if (kernel != 0 && kernel != v.kernel) {
         v.kernel = kernel;
-        v.heads_wg = kernel == SA_KERNEL_WIDE ? 64 : 16;
+        v.heads_wg = kernel == SA_KERNEL_DECODE ? 16 : 64;
         set_splits(v, topk, 1);
     }
     if (splits > 0) set_splits(v, topk, splits);
@@ -1270,6 +1569,13 @@ sa_status resolve_variant(int64_t nq, int32_t h, int32_t topk, int32_t kernel, i
 template <int D, bool FUSED>
 hipError_t launch_wide(const AttnParams &p, hipStream_t stream) {
     hipLaunchKernelGGL((sa_attn_wide<D, FUSED>), dim3((unsigned)p.total_wg), dim3(WideCfg<D>::THREADS), 0, stream,
+                       p);
+    return hipGetLastError();
+}
+
+template <int D, bool FUSED>
+hipError_t launch_pair(const AttnParams &p, hipStream_t stream) {
+    hipLaunchKernelGGL((sa_attn_pair<D, FUSED>), dim3((unsigned)p.total_wg), dim3(PairCfg<D>::THREADS), 0, stream,
                        p);
     return hipGetLastError();
 }
@@ -1303,6 +1609,14 @@ hipError_t launch_attn(const AttnParams &p, const Variant &v, int32_t d, hipStre
         }
     }
     if (KV8) return hipErrorNotSupported;  // (resolve_variant keeps kv8 on the decode kernel)
+    if (v.kernel == SA_KERNEL_PAIR) {
+        switch (d) {
+            case 64: return launch_pair<64, FUSED>(p, hs);
+            case 128: return launch_pair<128, FUSED>(p, hs);
+            case 256: return launch_pair<256, FUSED>(p, hs);
+            default: return launch_pair<512, FUSED>(p, hs);
+        }
+    }
     switch (d) {
         case 64: return launch_wide<64, FUSED>(p, hs);
         case 128: return launch_wide<128, FUSED>(p, hs);
@@ -1347,7 +1661,7 @@ AttnParams base_params(const uint16_t *q, const uint16_t *kv, const float *sink,
 
 template <bool FUSED, bool KV8>
 sa_status enqueue(AttnParams &p, const Variant &v, int32_t d, hipStream_t hs) {
-    // decode kernel: one block per workgroup; wide kernel: 8 * ceil(nq / 8) queries' worth
+    // decode kernel: one block per workgroup; wide and pair kernels: 8 * ceil(nq / 8) queries' worth
     const int64_t units = v.kernel == SA_KERNEL_DECODE ? (int64_t)p.nq : 8 * (((int64_t)p.nq + 7) / 8);
     const int64_t total = units * p.n_hg * v.n_sp;
     if (total > 0x7fffffffLL) return SA_ERR_SHAPE;
@@ -1404,7 +1718,7 @@ void set_rope(AttnParams &p, const Rope &r) {
 // kv8 rows are read by the decode kernel only (it walks lists of any length)
 sa_status resolve_variant_kv(int64_t nq, int32_t h, int32_t topk, int32_t kernel, int32_t splits, bool kv8,
                              Variant *out) {
-    if (kv8 && kernel == SA_KERNEL_WIDE) return SA_ERR_UNSUPPORTED;
+    if (kv8 && (kernel == SA_KERNEL_WIDE || kernel == SA_KERNEL_PAIR)) return SA_ERR_UNSUPPORTED;
     return resolve_variant(nq, h, topk, kv8 ? SA_KERNEL_DECODE : kernel, splits, out);
 }
 

@@ -72,7 +72,7 @@ def test_decode_step_argument_checks(lib):
     assert f(None, None, None, None, None, None, 0, 4, 64, 8, 8, 0, 5, 0.1, None, None, 0, None, 0, 0) == sa.SA_OK
     assert f(None, None, None, None, None, None, 2, 4, 64, 8, 8, 0, 5, 0.1, None, None, 0, None, 0, 0) == \
         sa.SA_ERR_NULL
-    assert f(None, None, None, None, None, None, 2, 4, 64, 8, 8, 0, 5, 0.1, None, None, 0, None, 3, 0) in \
+    assert f(None, None, None, None, None, None, 2, 4, 64, 8, 8, 0, 5, 0.1, None, None, 0, None, 4, 0) in \
         (sa.SA_ERR_NULL, sa.SA_ERR_UNSUPPORTED)
     assert lib.sa_sparse_attn_decode_step_workspace_bytes(2, 4, 96, 8, 0, 0, 0) == 0
     assert lib.sa_sparse_attn_decode_step_workspace_bytes(64, 64, 512, 128, 0, 0, 0) == 0

@@ -103,7 +103,7 @@ CASES = [
     (7, 2, 128, 512, 128, 4096, 2048, 5000), # decode + compressed (long list)
     (8, 1, 64, 512, 128, 1000, 900, 129),    # compressed with the ring wrapped once
 ]
-VARIANTS = [None, (1, 1), (1, 3), (2, 1), (2, 2), (2, 5)]
+VARIANTS = [None, (1, 1), (1, 3), (2, 1), (2, 2), (2, 5), (3, 1), (3, 3)]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"case{c[0]}" for c in CASES])
@@ -120,7 +120,7 @@ def test_decode_step_vs_oracle(case, variant):
 
 
 @pytest.mark.parametrize("case", CASES[:4] + CASES[5:7], ids=[f"case{c[0]}" for c in CASES[:4] + CASES[5:7]])
-@pytest.mark.parametrize("variant", [(1, 1), (2, 1), (2, 3), (1, 2)], ids=str)
+@pytest.mark.parametrize("variant", [(1, 1), (2, 1), (2, 3), (1, 2), (3, 1), (3, 2)], ids=str)
 def test_decode_step_equals_separate_calls(case, variant):
     seed, b, h, d, W, ncr, kc, pos = case
     c = make_case(seed, b, h, d, W, ncr, kc, pos)

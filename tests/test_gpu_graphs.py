@@ -41,7 +41,7 @@ def test_decode_step_graph_replays():
         _ = (st.q.float() * 2).sum().item()   # eager work between replays
 
 
-@pytest.mark.parametrize("variant", [(1, 1), (1, 3), (2, 1), (2, 2)], ids=lambda v: "k%d_sp%d" % v)
+@pytest.mark.parametrize("variant", [(1, 1), (1, 3), (2, 1), (2, 2), (3, 1), (3, 3)], ids=lambda v: "k%d_sp%d" % v)
 def test_attention_graph_replays_split_and_kernels(variant):
     c = wl.small_case(31, 3, 4, 64, 512, 700, 600, 0.1)
     q, kv, sink, idx = (c[k].cuda() for k in ("q", "kv", "sink", "idx"))

@@ -110,7 +110,7 @@ SMALL = [
     (12, 1, 1, 16, 128, 80, 70, 0.1),
     (13, 1, 1, 16, 256, 80, 70, 0.1),
 ]
-VARIANTS = [None, (1, 1), (1, 2), (1, 3), (1, 7), (2, 1), (2, 2), (2, 5)]
+VARIANTS = [None, (1, 1), (1, 2), (1, 3), (1, 7), (2, 1), (2, 2), (2, 5), (3, 1), (3, 2), (3, 5)]
 
 
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: f"s{c[0]}_h{c[3]}_d{c[4]}_k{c[6]}")
@@ -123,7 +123,7 @@ def test_sparse_attn_small(case, variant):
 
 
 @pytest.mark.parametrize("d", [64, 512])
-@pytest.mark.parametrize("variant", [None, (1, 1), (1, 2), (2, 1)], ids=lambda v: "auto" if v is None else "k%d_sp%d" % v)
+@pytest.mark.parametrize("variant", [None, (1, 1), (1, 2), (2, 1), (3, 1), (3, 2)], ids=lambda v: "auto" if v is None else "k%d_sp%d" % v)
 def test_sparse_attn_scores_outrunning_the_first_stage(d, variant):
     """The wide kernel takes the weights against the first max it sees and replays the
     list when a later stage outruns it by more than 2^32.  Rows built from one query's

@@ -85,7 +85,7 @@ ATTN_CASES = [
     (15, 1, 3, 16, 512, 64, 64, 512, 0),        # a table row of two copy instructions
     (16, 2, 2, 16, 512, 64, 50, 264, 3),        # ... the second one partial
 ]
-VARIANTS = [None, (1, 1), (1, 3), (2, 1), (2, 4)]
+VARIANTS = [None, (1, 1), (1, 3), (2, 1), (2, 4), (3, 1), (3, 3)]
 
 
 @pytest.mark.parametrize("case", ATTN_CASES, ids=[f"case{c[0]}" for c in ATTN_CASES])
