@@ -692,7 +692,10 @@ struct PairCfg {
     static constexpr float SLACK = 32.0f;
     static constexpr int PFK = D > 256 ? 2 : 4;
     static constexpr int PFV = D > 256 ? 2 : 3;
-    static constexpr int copy_at(int i) { return (i * RPW + KS - 1) / KS; }
+    // the next stage's copies go out over the first quarter of the score product
+    // (measured a little faster here than an even spread: two workgroups share
+    // the CU's memory pipeline, and the copies start their flight sooner)
+    static constexpr int copy_at(int i) { return std::min(RPW, (4 * i * RPW + KS - 1) / KS); }
     static_assert(KS >= 4 && DT >= 2 && RPW == 16, "tiling");
 };
 
@@ -729,22 +732,24 @@ __global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const Att
     // the first index chunk goes in flight before anything else: it heads the critical path
     Compactor<C::THREADS, C::LIST_CAP> cmp;
     cmp.load(fetch, lo, min(hi, lo + C::LIST_CAP));
-
-    // Q as the B operand, straight from memory: lane (hf, n) holds
-    // q[head n][16 ks + 8 hf .. +8] for every ks (zeros past h)
     const int head = ((int)hg * 2 + wave) * 32 + n;
     const bool head_ok = head < p.h;
-    bf16x8_t qreg[C::KS];
-    {
-        const uint16_t *qrow = p.q + ((int64_t)qi * p.h + (head_ok ? head : 0)) * D + 8 * hf;
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(qrow + 16 * ks);
-            qreg[ks] = __builtin_bit_cast(bf16x8_t, head_ok ? v : u32x4_t{0u, 0u, 0u, 0u});
-        }
-    }
+    // the head's sink, ahead of any copy (a load issued behind the copies waits for them)
+    const float sink_any = p.sink[min(head, p.h - 1)];
 
     cmp.ready();
+    // Q rows: wave w copies its own 32 head rows (one 1 KiB row per wave
+    // instruction) into rows 32 w .. 32 w + 31 of the stage buffers, to be read
+    // into registers once the list is packed; a head past h takes row 0 of the
+    // query (its column of S and O is never stored)
+    const uint32_t smem_base = lds_addr((const SA_LDS void *)smem);
+#pragma unroll 1
+    for (int u = 0; u < 32; ++u) {
+        const int hd = ((int)hg * 2 + wave) * 32 + u;
+        if (chunk_lane)
+            dma_16B(p.q + ((int64_t)qi * p.h + (hd < p.h ? hd : 0)) * D + lane * 8,
+                    smem_base + (uint32_t)((wave * 32 + u) * C::RS));
+    }
     if (has_new && wave == 0) {
         // the new row rounded through fp8 into its ring slot (as in the wide kernel)
         const u32x4_t r = fp8_round_trip_chunk(new_raw);
@@ -753,7 +758,6 @@ __global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const Att
         asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
     }
 
-    const uint32_t smem_base = lds_addr((const SA_LDS void *)smem);
     const bool rot = p.rope != nullptr && p.n_sp == 1;
     if (rot && wave == 0) copy_rope_row(p, qi, lane, lds_addr((const SA_LDS void *)rtab));
     const SA_LDS char *lds = (const SA_LDS char *)smem;
@@ -765,6 +769,8 @@ __global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const Att
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) acc_o[dt] = f32x16_t{};
     if (tid == 0) replay[0] = replay[1] = 0;  // read only after the barriers of pack
+    // Q as the B operand: lane (hf, n) holds q[head n][16 ks + 8 hf .. +8] for every ks
+    bf16x8_t qreg[C::KS];
 
     const uint16_t *kvb = p.kv + (int64_t)bi * p.rows * D;
     const int koff = n * C::RS + 16 * hf;
@@ -783,6 +789,14 @@ __global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const Att
         if (FUSED && first_pass && hg == 0 && p.idx_out) cmp.store(p.idx_out + (int64_t)qi * p.topk, c0, c1);
         const int nv = cmp.pack(p.rows, list, wcnt);
         const int nst = (nv + C::ROWS - 1) / C::ROWS;
+        if (c0 == lo && first_pass) {
+            // this wave's head rows have landed: into registers, then free the buffers
+            asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ++ks)
+                qreg[ks] = lds_read_b128(lds + (wave * 32 + n) * C::RS + 32 * ks + 16 * hf);
+            lds_barrier();
+        }
         if (nv == 0) continue;
 
         // copies of stage st into buffer st % 2: this wave's RPW rows, one wave
@@ -924,7 +938,7 @@ __global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const Att
         }
         return;
     }
-    const float sink_l2 = head_ok ? p.sink[head] * kLog2e : 0.f;
+    const float sink_l2 = head_ok ? sink_any * kLog2e : 0.f;
     const float Lt = l_run + exp2_fast(sink_l2 - m_ref);
     const float inv = Lt > 0.f ? 1.0f / Lt : 0.f;
     lds_barrier();  // stage buffers free
@@ -941,13 +955,23 @@ __global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const Att
         }
     }
     lds_barrier();
-#pragma unroll 4
-    for (int hr = wave; hr < C::HEADS; hr += C::NW) {
-        const int hglob = (int)hg * C::HEADS + hr;
-        if (hglob < p.h && chunk_lane) {
-            u32x4_t v = *reinterpret_cast<const SA_LDS u32x4_t *>(stg + hr * C::RS + 16 * lane);
-            if (rot) v = unrotate_chunk(v, 8 * lane, D, p.rope_dim, (const SA_LDS float *)rtab);
-            *reinterpret_cast<u32x4_t *>(p.out + ((int64_t)qi * p.h + hglob) * D + lane * 8) = v;
+    // one head row per wave instruction (lane l: chunk l), in batches of 8 rows
+    // whose LDS reads all go out before their stores
+#pragma unroll 1
+    for (int r0 = wave; r0 < C::HEADS; r0 += 8 * C::NW) {
+        u32x4_t v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            v[i] = *reinterpret_cast<const SA_LDS u32x4_t *>(stg + (r0 + i * C::NW) * C::RS + 16 * lane);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int hr = r0 + i * C::NW;
+            const int hglob = (int)hg * C::HEADS + hr;
+            if (hglob < p.h && chunk_lane) {
+                u32x4_t w = v[i];
+                if (rot) w = unrotate_chunk(w, 8 * lane, D, p.rope_dim, (const SA_LDS float *)rtab);
+                *reinterpret_cast<u32x4_t *>(p.out + ((int64_t)qi * p.h + hglob) * D + lane * 8) = w;
+            }
         }
     }
 }
