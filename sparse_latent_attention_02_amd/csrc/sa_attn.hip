@@ -306,7 +306,7 @@ struct WideCfg {
     static_assert(KS >= 4 && DT >= 2 && DT % 2 == 0 && RPW == 16, "tiling");
 };
 
-template <int D, bool FUSED>
+template <int D, bool FUSED, bool SPLIT>
 __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const AttnParams p) {
     using C = WideCfg<D>;
     __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
@@ -576,7 +576,7 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
     const float f_o = exp2_fast(m_o - M);
     const float Ls = l_run * f_s + l_o * f_o;
     constexpr int DH2 = C::DT / 2;
-    const bool split = p.n_sp > 1;
+    constexpr bool split = SPLIT;  // (a template parameter: the split-free build keeps no partial-store code)
     // output = (own O f_s + partner's O f_o) / (Ls + sink term); split partials
     // keep O unnormalised against M
     float a_s = f_s, a_o = f_o;
@@ -699,7 +699,7 @@ struct PairCfg {
     static_assert(KS >= 4 && DT >= 2 && RPW == 16, "tiling");
 };
 
-template <int D, bool FUSED>
+template <int D, bool FUSED, bool SPLIT>
 __global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const AttnParams p) {
     using C = PairCfg<D>;
     __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
@@ -921,16 +921,18 @@ __global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const Att
     // ---- sink fold + normalise (or f32 partials), stage bf16 rows, store a row per instruction ----
     l_run += shfl_xor_f32(l_run, 32);  // the head's sum over all rows
     asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
-    const bool split = p.n_sp > 1;
+    constexpr bool split = SPLIT;  // (a template parameter: the split-free build keeps no partial-store code)
     if (split) {
         if (head_ok) {
             const int64_t prow = ((int64_t)qi * p.n_sp + sp) * p.h + head;
 #pragma unroll
-            for (int k = 0; k < C::DT; ++k)
+            for (int k = 0; k < C::DT; ++k) {
 #pragma unroll
                 for (int qd = 0; qd < 4; ++qd)
                     *reinterpret_cast<f32x4_t *>(p.part_o + prow * D + 32 * k + 8 * qd + 4 * hf) =
                         f32x4_t{acc_o[k][4 * qd], acc_o[k][4 * qd + 1], acc_o[k][4 * qd + 2], acc_o[k][4 * qd + 3]};
+                __builtin_amdgcn_sched_barrier(0);  // one tile out of the accumulators at a time
+            }
             if (hf == 0) {
                 p.part_ml[prow * 2] = m_ref;
                 p.part_ml[prow * 2 + 1] = l_run;
@@ -953,6 +955,9 @@ __global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const Att
                 u32x2_t{pack_bf16x2(w[4 * qd] * inv, w[4 * qd + 1] * inv),
                         pack_bf16x2(w[4 * qd + 2] * inv, w[4 * qd + 3] * inv)};
         }
+        // one tile out of the accumulators at a time: reads of all of them hoisted
+        // ahead would need as many vector registers again and spill
+        __builtin_amdgcn_sched_barrier(0);
     }
     lds_barrier();
     // one head row per wave instruction (lane l: chunk l), in batches of 8 rows
@@ -1592,15 +1597,23 @@ sa_status resolve_variant(int64_t nq, int32_t h, int32_t topk, int32_t kernel, i
 
 template <int D, bool FUSED>
 hipError_t launch_wide(const AttnParams &p, hipStream_t stream) {
-    hipLaunchKernelGGL((sa_attn_wide<D, FUSED>), dim3((unsigned)p.total_wg), dim3(WideCfg<D>::THREADS), 0, stream,
-                       p);
+    if (p.n_sp > 1)
+        hipLaunchKernelGGL((sa_attn_wide<D, FUSED, true>), dim3((unsigned)p.total_wg), dim3(WideCfg<D>::THREADS), 0,
+                           stream, p);
+    else
+        hipLaunchKernelGGL((sa_attn_wide<D, FUSED, false>), dim3((unsigned)p.total_wg), dim3(WideCfg<D>::THREADS), 0,
+                           stream, p);
     return hipGetLastError();
 }
 
 template <int D, bool FUSED>
 hipError_t launch_pair(const AttnParams &p, hipStream_t stream) {
-    hipLaunchKernelGGL((sa_attn_pair<D, FUSED>), dim3((unsigned)p.total_wg), dim3(PairCfg<D>::THREADS), 0, stream,
-                       p);
+    if (p.n_sp > 1)
+        hipLaunchKernelGGL((sa_attn_pair<D, FUSED, true>), dim3((unsigned)p.total_wg), dim3(PairCfg<D>::THREADS), 0,
+                           stream, p);
+    else
+        hipLaunchKernelGGL((sa_attn_pair<D, FUSED, false>), dim3((unsigned)p.total_wg), dim3(PairCfg<D>::THREADS), 0,
+                           stream, p);
     return hipGetLastError();
 }
 
