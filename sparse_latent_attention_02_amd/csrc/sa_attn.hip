@@ -1,5 +1,5 @@
-// sa_attn.hip -- sparse latent attention for CDNA4 (gfx950): the wide kernel,
-// the split combine and the dispatcher.
+// sa_attn.hip -- sparse latent attention for CDNA4 (gfx950): the pair, wide
+// and decode kernels, the split combine and the dispatcher.
 //
 // Operation ("DeepSeek V4.1 ... attention / attend": sparse_attn_kernel and its
 // wrapper; "Module attn" rustdoc: sparse_attn): for every query and head, a
@@ -8,29 +8,36 @@
 // One latent row is both key and value and is shared by every head, so a
 // workgroup gathers each selected row into LDS once and all its heads use it.
 //
-// Wide kernel: one workgroup per (query, group of 64 heads[, index split]);
-// each wavefront owns 32 heads, over the whole head dim up to d = 256 and over
-// half of it at d = 512 (a wavefront pair then sums its partial scores through
-// LDS before the softmax).
+// Three kernels share the operation; the dispatcher picks one from the shape.
+//  * pair kernel (prefill-sized grids): one workgroup of two wavefronts per
+//    (query, 64 heads[, index split]); each wavefront holds a 32-head tile over
+//    the whole head dim and walks every row of the list in 32-row stages, so no
+//    merge between wavefronts; under 80 KiB of LDS, two workgroups per CU.
+//  * wide kernel (long lists in decode-sized grids): four wavefronts per
+//    (query, 64 heads[, split]) as 2 head tiles x 2 halves of every 64-row
+//    stage; the halves are merged once at the end.
+//  * decode kernel (short lists, decode-sized grids): four wavefronts per
+//    (query, 16 heads[, split]), see its own header below.
+// The wide and pair kernels:
 //  1. compaction: the query's index entries are scanned and the valid ones
 //     (0 <= idx < rows) packed into an LDS list, so -1 entries cost no MFMA work
 //     and no traffic;
-//  2. gather: 32-row stages copied HBM -> LDS with the direct global->LDS path
-//     (16 B per lane, one 1 KiB row per wave instruction at d = 512),
-//     double-buffered so the copy of stage t+1 overlaps the maths of stage t.
-//     LDS rows are padded by 48 bytes, which keeps both operand reads of steps 3
-//     and 5 free of bank conflicts and makes every operand address a per-lane
-//     base plus an immediate;
+//  2. gather: stages of rows copied HBM -> LDS with the direct global->LDS path
+//     (16 B per lane, one 1 KiB row per wave instruction at d = 512), two
+//     buffers, so the copy of stage t+1 overlaps the maths of stage t.  LDS rows
+//     are padded by 48 bytes, which keeps the score operand reads free of bank
+//     conflicts and makes every operand address a per-lane base plus an
+//     immediate;
 //  3. scores S^T[32 rows][32 heads] = K[rows][:] . Q[heads][:]^T on MFMA
 //     32x32x16 bf16 (A = gathered rows from LDS, B = the wave's Q held in
-//     registers for the whole kernel), f32 accumulation;
-//  4. online softmax in the base-2 domain (scale * log2 e folded once).  The
-//     accumulator layout puts one head per lane column, so the running max
-//     needs one cross-lane step.  The running max is only moved (and O, l
-//     rescaled) when a stage's max exceeds it by more than 2^8, so most stages
-//     skip the rescale; weights stay <= 256, well inside bf16's range.  It
-//     starts at the finite -1e30 of the pages' kernel, so a list with no valid
-//     entry yields zeros rather than NaN;
+//     registers for the whole list), f32 accumulation;
+//  4. softmax in the base-2 domain (scale * log2 e folded once) against a fixed
+//     reference max: the first stage max a wavefront sees.  A later stage max may
+//     exceed it by up to 2^32 (weights stay far inside bf16 and f32 range), so O
+//     is never rescaled inside the loop; should one outrun it further, the
+//     workgroup replays the list against the larger max.  The reference starts
+//     at the finite -1e30 of the pages' kernel, so a list with no valid entry
+//     yields zeros rather than NaN;
 //  5. O^T[d][head] += V^T[d][rows] . P^T[rows][head] on the same MFMA: P is
 //     rounded to bf16 straight from the score registers (its lane layout is the
 //     B operand's, up to a permutation of the contraction index that the V^T
