@@ -60,6 +60,9 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kListCap = 4096;        // compacted entries held in LDS at once
 constexpr float kRescaleSlack = 8.0f; // log2 units the reference max may lag behind
+#ifndef SA_PFV_EARLY
+#define SA_PFV_EARLY 1
+#endif
 
 struct AttnParams {
     const uint16_t *q;
@@ -133,6 +136,17 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const SA_LDS char *p) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// max / sum of v over lanes l and l ^ 32 (gfx950 v_permlane32_swap: a VALU
+// exchange of the wave's halves, no LDS round trip)
+__device__ __forceinline__ float max_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Wait until at most n (wave-uniform, 0..16) vector-memory operations of this
 // wave are outstanding; the count is an immediate of the instruction, so the
 // value selects one of the fixed waits.
@@ -198,6 +212,45 @@ __device__ __forceinline__ bool wide_unit(const AttnParams &p, uint32_t &qi, uin
     qi = 8u * (rounds - 1u - m) + (blockIdx.x & 7u);
     return qi < (uint32_t)p.nq;
 }
+
+// Stage-buffer row layout of the wide and pair kernels.  A gathered row of D
+// bf16 values takes RS = 2 D + 64 bytes of LDS, and its 16-byte chunk c sits
+// in slot c ^ swz(r) of row r, swz(r) = (r >> 2) & 3 (the chunks of each
+// aligned group of four trade places).  The LDS serves 64 banks of 4 bytes:
+//  * score operand reads (16 B a lane, 16 lanes a cycle: 16 consecutive rows,
+//    one chunk): RS puts row r at bank offset 64 r mod 256 bytes, four rows
+//    apart coinciding; the swizzle moves those four to four different chunks;
+//  * transposing reads of the weighted-sum operand (8 B a lane, 32 lanes a
+//    cycle: 4 consecutive rows sharing swz, 4 aligned chunks each): the rows'
+//    64-byte spans sit 64 B apart, the swizzle only permutes chunks inside a
+//    span -- conflict-free as well (the unswizzled 48-byte padding served
+//    these at half rate).
+// The direct copy writes a row's chunks contiguously, so the swizzle is taken
+// on the global side: lane i copies chunk i ^ swz(r).
+template <int D>
+struct RowLayout {
+    static constexpr int RS = 2 * D + 64;
+    static_assert(RS % 64 == 0 && (RS / 64) % 2 == 1, "row stride: an odd multiple of 64 bytes");
+    static constexpr int OUT_RS = 2 * D + 16;  // bf16 output staging rows (written 8 B a lane, read whole)
+    __device__ static __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+    // per-lane bases of the score operand reads: lane (hf, n) reads chunk
+    // 2 ks + hf of row r; k-steps alternate between the two bases, 64 B apart
+    // per pair of k-steps (chunk 2 ks + hf ^ swz = 4 (ks >> 1) + ((2 (ks & 1) + hf) ^ swz))
+    __device__ static __forceinline__ int kbase(int r, int hf) { return r * RS + 16 * (hf ^ swz(r)); }
+    __device__ static __forceinline__ int koff(int kb_even, int ks) {
+        return (ks & 1 ? kb_even ^ 32 : kb_even) + 64 * (ks >> 1);
+    }
+    // per-lane bases of the transposing reads: the 16-lane group reads rows
+    // r0 + 4 hf + p/4 (rows of a block of 16, +8 for the upper half of the
+    // contraction index) and, within each 64-byte span, chunk 2 (lane bit 4) +
+    // (p bit 1), half p bit 0 (p = lane % 16)
+    __device__ static __forceinline__ int vbase(int r0, int lane, bool upper) {
+        const int hf = lane >> 5, p16 = lane & 15;
+        const int r = r0 + 4 * hf + (p16 >> 2) + (upper ? 8 : 0);
+        const int c = 2 * ((lane >> 4) & 1) + ((p16 >> 1) & 1);
+        return r * RS + 16 * (c ^ swz(r)) + 8 * (p16 & 1);
+    }
+};
 
 // Index-list compaction.  The entries of idx[c0, c1) (at most CAP) are
 // spread over the workgroup's threads as e = c0 + k * NT + tid, k < K, and all
@@ -268,6 +321,102 @@ struct Compactor {
     }
 };
 
+// Weights of one wavefront's 32-row slice of a stage, and its share of the
+// weighted sum O^T[d][32 heads] += V^T P^T (wide and pair kernels).
+//  * Score value i of lane (hf, n) is slice row 8 (i / 4) + 4 hf + i % 4,
+//    head n; rows at or past the list end (entry ebase + row >= nv) weigh 0.
+//  * Weights are 2^(scale log2(e) s - m_ref) against a fixed reference: the
+//    first slice holding a valid row sets m_ref to its own max.  Later slices
+//    take their weights at once and compare their max with the reference only
+//    behind the first MFMA of the weighted sum: a max past it by more than
+//    SLACK (weights up to 2^SLACK stay far inside bf16 and f32 range) raises
+//    the replay flag, and the workgroup replays the list against the larger
+//    max, so O is never rescaled inside the loop.
+//  * The running sum adds the weights as rounded to bf16, as the MFMA takes them.
+//  * The first operand reads of the weighted sum go out before the weights:
+//    they do not depend on them.  MFMA j = kk DT + dt reads, in 16-lane group
+//    (hf, column half), rows 16 kk + 8 rd + 4 hf + p / 4 (rd = 0, 1) and
+//    columns 32 dt + 16 (column half) + 4 (p % 4), p = lane % 16, through the
+//    transposing read; P enters from the score registers (its lane layout is
+//    the B operand's up to the matching permutation of the contraction index).
+template <class C>
+__device__ __forceinline__ void slice_weights_pv(const f32x16_t &sacc, int ebase, int nv, float scale_log2,
+                                                 float &m_ref, float &m_seen, float &l_run, bool &have_ref,
+                                                 int &replay_flag, const SA_LDS char *buf, int vlo, int vhi,
+                                                 f32x16_t (&acc_o)[C::DT]) {
+    const int lane = threadIdx.x & 63;
+    const int hf = lane >> 5;
+    auto vread = [&](int j) {
+        const int dt = j % C::DT, kk = j / C::DT;
+        const i16x4_t lo4 = lds_read_tr16(buf + vlo + (16 * kk) * C::RS + 64 * dt);
+        const i16x4_t hi4 = lds_read_tr16(buf + vhi + (16 * kk) * C::RS + 64 * dt);
+        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    constexpr int NJ = 2 * C::DT;
+    constexpr int PF = C::PFV;
+    bf16x8_t vq[PF];
+#pragma unroll
+    for (int i = 0; i < C::PFV_EARLY; ++i) vq[i] = vread(i);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // rows of a last, partial slice past the list end (partial is wave-uniform)
+    const bool partial = ebase + 32 > nv;
+    auto valid = [&](int i) { return ebase + 8 * (i >> 2) + 4 * hf + (i & 3) < nv; };
+    const bool check = have_ref;
+    if (!have_ref && ebase < nv) {
+        // the first slice with a valid row: the reference is its max
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, partial && !valid(i) ? -INFINITY : sacc[i] * scale_log2);
+        m_ref = m_seen = max_xor32(mx);
+        have_ref = true;
+    }
+    // exponents t = scale log2(e) s - m_ref (-inf for rows past the list end)
+    // and their max, which checks the reference behind the first MFMA below
+    float mt = -INFINITY;
+    uint32_t pk[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float t0 = fmaf(sacc[2 * i], scale_log2, -m_ref);
+        float t1 = fmaf(sacc[2 * i + 1], scale_log2, -m_ref);
+        if (partial) {
+            t0 = valid(2 * i) ? t0 : -INFINITY;
+            t1 = valid(2 * i + 1) ? t1 : -INFINITY;
+        }
+        mt = fmaxf(mt, fmaxf(t0, t1));
+        pk[i] = pack_bf16x2(exp2_fast(t0), exp2_fast(t1));
+    }
+    const bf16x8_t pb0 = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
+    const bf16x8_t pb1 = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[4], pk[5], pk[6], pk[7]});
+#pragma unroll
+    for (int i = C::PFV_EARLY; i < PF; ++i) vq[i] = vread(i);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const bf16x8_t a = vq[j % PF];
+        if (j + PF < NJ) vq[j % PF] = vread(j + PF);
+        acc_o[j % C::DT] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, j >= C::DT ? pb1 : pb0, acc_o[j % C::DT], 0, 0, 0);
+        if (j == 0 && check) {
+            // a slice max past the reference by more than SLACK: replay against the larger max
+            mt = max_xor32(mt);
+            m_seen = fmaxf(m_seen, m_ref + mt);
+            if (__ballot(mt > C::SLACK)) {
+                if (lane == 0) replay_flag = 1;
+                m_ref = m_seen;
+            }
+        }
+        // the running sum over the weights behind MFMAs 1 .. NJ-1, in order
+        if (j >= 1) {
+#pragma unroll
+            for (int k = (j - 1) * 8 / (NJ - 1); k < j * 8 / (NJ - 1); ++k) {
+                const uint32_t b = pk[k];
+                l_run += __uint_as_float(b << 16) + __uint_as_float(b & 0xffff0000u);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 template <int D>
 struct WideCfg {
     // Four wavefronts: 2 head tiles of 32 heads x 2 row halves of every 64-row
@@ -281,12 +430,10 @@ struct WideCfg {
     static constexpr int HEADS = 64;
     static constexpr int ROWS = 64;               // rows per stage (32 per wavefront)
     static constexpr int RPW = ROWS / NW;         // rows each wavefront copies per stage
-    static constexpr int ROW_BYTES = 2 * D;
-    // LDS row stride: 3 spare 16-byte chunks per row put row r's chunk c at bank
-    // position (3 r + c) mod 16, distinct for the 16 rows of an operand fetch and
-    // for the 4 rows x 2 chunks of a transposing read -- and every operand
-    // address is a per-lane base plus a compile-time offset
-    static constexpr int RS = ROW_BYTES + 48;
+    using L = RowLayout<D>;
+    // stage rows in the swizzled layout of RowLayout: every operand address is
+    // one of a few per-lane bases plus a compile-time offset
+    static constexpr int RS = L::RS;
     static constexpr int CH = D / 8;              // 16-byte chunks per row
     static constexpr int KS = D / 16;             // k-steps of the score product
     static constexpr int DT = D / 32;             // 32-wide d tiles of the output
@@ -298,6 +445,7 @@ struct WideCfg {
     static constexpr float SLACK = 32.0f;
     static constexpr int PFK = D > 256 ? 2 : 4;
     static constexpr int PFV = D > 256 ? 2 : 3;
+    static constexpr int PFV_EARLY = SA_PFV_EARLY;  // weighted-sum operand reads issued ahead of the weights
     // The next stage's copies are spread evenly over the KS MFMAs of the score
     // product: a wave's memory instructions issue only as fast as the memory
     // pipeline drains, and a wave held up issuing a block of them leaves its MFMA
@@ -308,9 +456,9 @@ struct WideCfg {
     static constexpr int NR = DT / 2 > 1 ? 2 : 1;
     static constexpr int TPR = DT / 2 / NR;
     static constexpr int XR_BYTES = NW * TPR * 64 * 64;
-    static constexpr int OUT_BYTES = HEADS * RS;  // staged bf16 output of the workgroup
+    static constexpr int OUT_BYTES = HEADS * L::OUT_RS;  // staged bf16 output of the workgroup
     static constexpr int SMEM = std::max(NBUF * STAGE_BYTES, XR_BYTES + OUT_BYTES);
-    static_assert(KS >= 4 && DT >= 2 && DT % 2 == 0 && RPW == 16, "tiling");
+    static_assert(KS >= 4 && DT >= 2 && DT % 2 == 0 && RPW == 16 && PFV_EARLY <= PFV, "tiling");
 };
 
 template <int D, bool FUSED, bool SPLIT>
@@ -382,7 +530,8 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
         const int hl = wave * C::RPW + u;
         const int hd = (int)hg * C::HEADS + hl;
         if (hd < p.h) {
-            if (chunk_lane) dma_16B(p.q + ((int64_t)qi * p.h + hd) * D + lane * 8, smem_base + hl * C::RS);
+            if (chunk_lane)
+                dma_16B(p.q + ((int64_t)qi * p.h + hd) * D + (lane ^ C::L::swz(hl)) * 8, smem_base + hl * C::RS);
         } else if (chunk_lane) {
             *reinterpret_cast<SA_LDS u32x4_t *>((SA_LDS char *)smem + hl * C::RS + 16 * lane) =
                 u32x4_t{0u, 0u, 0u, 0u};
@@ -394,6 +543,7 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
     float m_ref = -1e30f;   // fixed reference max (log2 domain) the weights are taken against
     float m_seen = -1e30f;  // largest stage max seen
     float l_run = 0.0f;     // this lane's share of the running sum
+    bool have_ref = false;  // m_ref set (wave-uniform)
     f32x16_t acc_o[C::DT];
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) acc_o[dt] = f32x16_t{};
@@ -401,10 +551,9 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
 
     const uint16_t *kvb = p.kv + (int64_t)bi * p.rows * D;
     // per-lane operand bases inside a stage buffer (see the two read patterns below)
-    const int koff = (32 * rh + n) * C::RS + 16 * hf;
-    const int p16 = lane & 15;
-    const int voff = (32 * rh + 4 * hf + (p16 >> 2)) * C::RS + 16 * (2 * ((lane >> 4) & 1) + ((p16 & 3) >> 1)) +
-                     ((p16 & 1) << 3);
+    const int kb = C::L::kbase(32 * rh + n, hf);
+    const int vlo = C::L::vbase(32 * rh, lane, false);
+    const int vhi = C::L::vbase(32 * rh, lane, true);
 
 
     // The weights are taken against a fixed reference: the first stage max a wave
@@ -437,7 +586,7 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
             const uint32_t buf = smem_base + (uint32_t)(((st + 1) & 1) * C::STAGE_BYTES + wave * C::RPW * C::RS);
             for (int u = u0; u < u1; ++u) {
                 const int row = __builtin_amdgcn_readlane(rows_reg, u);
-                if (chunk_lane) dma_16B(kvb + (int64_t)row * D + lane * 8, buf + u * C::RS);
+                if (chunk_lane) dma_16B(kvb + (int64_t)row * D + (lane ^ C::L::swz(wave * C::RPW + u)) * 8, buf + u * C::RS);
             }
         };
         if (nv > 0) {
@@ -455,7 +604,7 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
             lds_barrier();
 #pragma unroll
             for (int ks = 0; ks < C::KS; ++ks)
-                qreg[ks] = lds_read_b128(lds + (hw * 32 + n) * C::RS + 32 * ks + 16 * hf);
+                qreg[ks] = lds_read_b128(lds + C::L::koff(C::L::kbase(hw * 32 + n, hf), ks));
         }
         if (nv == 0) continue;
 
@@ -473,81 +622,23 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
             //      the scheduling barriers keep the compiler from hoisting the reads ----
             f32x16_t sacc = {};
             {
-                const SA_LDS char *kb = buf + koff;
                 constexpr int PF = C::PFK;
                 bf16x8_t kq[PF];
 #pragma unroll
-                for (int i = 0; i < PF; ++i) kq[i] = lds_read_b128(kb + 32 * i);
+                for (int i = 0; i < PF; ++i) kq[i] = lds_read_b128(buf + C::L::koff(kb, i));
 #pragma unroll
                 for (int ks = 0; ks < C::KS; ++ks) {
                     const bf16x8_t a = kq[ks % PF];
-                    if (ks + PF < C::KS) kq[ks % PF] = lds_read_b128(kb + 32 * (ks + PF));
+                    if (ks + PF < C::KS) kq[ks % PF] = lds_read_b128(buf + C::L::koff(kb, ks + PF));
                     if (more) copy_rows(st + 1, rows_next, C::copy_at(ks), C::copy_at(ks + 1));
                     sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc, 0, 0, 0);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
 
-            // ---- softmax: value i of lane (hf, n) is row 8(i/4) + 4 hf + i%4 of this
-            //      wave's half, head n ----
-            const int ebase = st * C::ROWS + 32 * rh;
-            f32x16_t &sv = sacc;  // scores in the base-2 domain, in place
-            float mx = -INFINITY;
-            if (ebase + 32 <= nv) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    sv[i] = sacc[i] * p.scale_log2;
-                    mx = fmaxf(mx, sv[i]);
-                }
-            } else {  // last, partial stage: rows past the list end weigh nothing
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int r = 8 * (i >> 2) + 4 * hf + (i & 3);
-                    sv[i] = ebase + r < nv ? sacc[i] * p.scale_log2 : -INFINITY;
-                    mx = fmaxf(mx, sv[i]);
-                }
-            }
-            mx = fmaxf(mx, shfl_xor_f32(mx, 32));
-            m_seen = fmaxf(m_seen, mx);
-            if (__ballot(mx > m_ref + C::SLACK)) {
-                if (__ballot(m_ref > -1e29f) && lane == 0) replay[st & 1] = 1;
-                m_ref = m_seen;
-            }
-            uint32_t pk[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t b = pack_bf16x2(exp2_fast(sv[2 * i] - m_ref), exp2_fast(sv[2 * i + 1] - m_ref));
-                pk[i] = b;
-                l_run += __uint_as_float(b << 16) + __uint_as_float(b & 0xffff0000u);
-            }
-            const bf16x8_t pb0 = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
-            const bf16x8_t pb1 = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[4], pk[5], pk[6], pk[7]});
-
-            // ---- O^T += V^T P^T.  MFMA j = kk DT + dt; for it, the 16-lane group
-            //      (hf, column half) reads rows 16 kk + 8 rd + 4 hf + p/4 (rd = 0, 1) of this
-            //      wave's half, columns 32 dt + 16 (column half) + 4 (p%4), p = lane % 16 ----
-            {
-                const SA_LDS char *vb = buf + voff;
-                auto vread = [&](int j) {
-                    const int dt = j % C::DT, kk = j / C::DT;
-                    const i16x4_t lo4 = lds_read_tr16(vb + (16 * kk) * C::RS + 64 * dt);
-                    const i16x4_t hi4 = lds_read_tr16(vb + (16 * kk + 8) * C::RS + 64 * dt);
-                    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-                };
-                constexpr int NJ = 2 * C::DT;
-                constexpr int PF = C::PFV;
-                bf16x8_t vq[PF];
-#pragma unroll
-                for (int i = 0; i < PF; ++i) vq[i] = vread(i);
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) {
-                    const bf16x8_t a = vq[j % PF];
-                    if (j + PF < NJ) vq[j % PF] = vread(j + PF);
-                    acc_o[j % C::DT] =
-                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, j >= C::DT ? pb1 : pb0, acc_o[j % C::DT], 0, 0, 0);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
+            // ---- weights and weighted sum of this wave's half of the stage ----
+            slice_weights_pv<C>(sacc, st * C::ROWS + 32 * rh, nv, p.scale_log2, m_ref, m_seen, l_run, have_ref,
+                                replay[st & 1], buf, vlo, vhi, acc_o);
         }
         lds_barrier();  // the last stage's flag is raised by now
         if (replay[0] | replay[1]) {
@@ -568,7 +659,7 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
     // ---- merge the two row halves of each head tile: M = max, O and l rescaled
     //      to M and added.  Wave rh finalises d tiles [rh DT/2, (rh+1) DT/2) and
     //      hands the other half of its O to its partner ----
-    l_run += shfl_xor_f32(l_run, 32);  // the head's sum over this wave's rows
+    l_run = sum_xor32(l_run);  // the head's sum over this wave's rows
     asm volatile("s_waitcnt vmcnt(0)" : : : "memory");  // (an empty list leaves the head-row copies running)
     lds_barrier();                     // stage buffers free
     if (hf == 0) {
@@ -633,7 +724,7 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
                                                          (((int64_t)qi * p.n_sp + sp) * p.h + head) * D +
                                                          32 * k + 8 * qd + 4 * hf) = o;
                     } else {
-                        *reinterpret_cast<SA_LDS u32x2_t *>(stg + (hw * 32 + n) * C::RS + 64 * k + 16 * qd + 8 * hf) =
+                        *reinterpret_cast<SA_LDS u32x2_t *>(stg + (hw * 32 + n) * C::L::OUT_RS + 64 * k + 16 * qd + 8 * hf) =
                             u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
                     }
                 }
@@ -659,7 +750,7 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
     for (int hr = wave; hr < C::HEADS; hr += C::NW) {
         const int hglob = (int)hg * C::HEADS + hr;
         if (hglob < p.h && chunk_lane) {
-            u32x4_t v = *reinterpret_cast<const SA_LDS u32x4_t *>(stg + hr * C::RS + 16 * lane);
+            u32x4_t v = *reinterpret_cast<const SA_LDS u32x4_t *>(stg + hr * C::L::OUT_RS + 16 * lane);
             if (rot) v = unrotate_chunk(v, 8 * lane, D, p.rope_dim, (const SA_LDS float *)rtab);
             *reinterpret_cast<u32x4_t *>(p.out + ((int64_t)qi * p.h + hglob) * D + lane * 8) = v;
         }
@@ -687,18 +778,20 @@ struct PairCfg {
     static constexpr int HEADS = 64;
     static constexpr int ROWS = 32;             // rows per stage (all of them, for each wavefront)
     static constexpr int RPW = ROWS / NW;       // rows each wavefront copies per stage
-    static constexpr int RS = 2 * D + 48;       // LDS row stride, as in the wide kernel
+    using L = RowLayout<D>;
+    static constexpr int RS = L::RS;            // stage rows as in the wide kernel
     static constexpr int CH = D / 8;
     static constexpr int KS = D / 16;
     static constexpr int DT = D / 32;
     static constexpr int STAGE_BYTES = ROWS * RS;
     static constexpr int NBUF = 2;
     static constexpr int LIST_CAP = 2048;       // compacted entries held at once
-    static constexpr int OUT_BYTES = HEADS * RS;  // staged bf16 output, over the stage buffers
+    static constexpr int OUT_BYTES = HEADS * L::OUT_RS;  // staged bf16 output, over the stage buffers
     static constexpr int SMEM = std::max(NBUF * STAGE_BYTES, OUT_BYTES);
     static constexpr float SLACK = 32.0f;
     static constexpr int PFK = D > 256 ? 2 : 4;
     static constexpr int PFV = D > 256 ? 2 : 3;
+    static constexpr int PFV_EARLY = SA_PFV_EARLY;  // weighted-sum operand reads issued ahead of the weights
     // the next stage's copies go out over the first quarter of the score product
     // (measured a little faster here than an even spread: two workgroups share
     // the CU's memory pipeline, and the copies start their flight sooner)
@@ -754,7 +847,7 @@ __global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const Att
     for (int u = 0; u < 32; ++u) {
         const int hd = ((int)hg * 2 + wave) * 32 + u;
         if (chunk_lane)
-            dma_16B(p.q + ((int64_t)qi * p.h + (hd < p.h ? hd : 0)) * D + lane * 8,
+            dma_16B(p.q + ((int64_t)qi * p.h + (hd < p.h ? hd : 0)) * D + (lane ^ C::L::swz(u)) * 8,
                     smem_base + (uint32_t)((wave * 32 + u) * C::RS));
     }
     if (has_new && wave == 0) {
@@ -772,6 +865,7 @@ __global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const Att
     float m_ref = -1e30f;
     float m_seen = -1e30f;
     float l_run = 0.0f;
+    bool have_ref = false;
     f32x16_t acc_o[C::DT];
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) acc_o[dt] = f32x16_t{};
@@ -780,10 +874,9 @@ __global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const Att
     bf16x8_t qreg[C::KS];
 
     const uint16_t *kvb = p.kv + (int64_t)bi * p.rows * D;
-    const int koff = n * C::RS + 16 * hf;
-    const int p16 = lane & 15;
-    const int voff = (4 * hf + (p16 >> 2)) * C::RS + 16 * (2 * ((lane >> 4) & 1) + ((p16 & 3) >> 1)) +
-                     ((p16 & 1) << 3);
+    const int kb = C::L::kbase(n, hf);
+    const int vlo = C::L::vbase(0, lane, false);
+    const int vhi = C::L::vbase(0, lane, true);
 
     // weights against a fixed reference max, with a whole-list replay should a
     // stage max outrun it by more than SLACK (see the wide kernel)
@@ -801,7 +894,7 @@ __global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const Att
             asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
 #pragma unroll
             for (int ks = 0; ks < C::KS; ++ks)
-                qreg[ks] = lds_read_b128(lds + (wave * 32 + n) * C::RS + 32 * ks + 16 * hf);
+                qreg[ks] = lds_read_b128(lds + C::L::koff(C::L::kbase(wave * 32 + n, hf), ks));
             lds_barrier();
         }
         if (nv == 0) continue;
@@ -817,7 +910,7 @@ __global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const Att
             const uint32_t buf = smem_base + (uint32_t)((st & 1) * C::STAGE_BYTES + wave * C::RPW * C::RS);
             for (int u = u0; u < u1; ++u) {
                 const int row = __builtin_amdgcn_readlane(rows_reg, u);
-                if (chunk_lane) dma_16B(kvb + (int64_t)row * D + lane * 8, buf + u * C::RS);
+                if (chunk_lane) dma_16B(kvb + (int64_t)row * D + (lane ^ C::L::swz(wave * C::RPW + u)) * 8, buf + u * C::RS);
             }
         };
         {
@@ -837,78 +930,23 @@ __global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const Att
             // ---- scores S^T[32 rows][32 heads]; the next stage's copies spread over them ----
             f32x16_t sacc = {};
             {
-                const SA_LDS char *kb = buf + koff;
                 constexpr int PF = C::PFK;
                 bf16x8_t kq[PF];
 #pragma unroll
-                for (int i = 0; i < PF; ++i) kq[i] = lds_read_b128(kb + 32 * i);
+                for (int i = 0; i < PF; ++i) kq[i] = lds_read_b128(buf + C::L::koff(kb, i));
 #pragma unroll
                 for (int ks = 0; ks < C::KS; ++ks) {
                     const bf16x8_t a = kq[ks % PF];
-                    if (ks + PF < C::KS) kq[ks % PF] = lds_read_b128(kb + 32 * (ks + PF));
+                    if (ks + PF < C::KS) kq[ks % PF] = lds_read_b128(buf + C::L::koff(kb, ks + PF));
                     if (more) copy_rows(st + 1, rows_next, C::copy_at(ks), C::copy_at(ks + 1));
                     sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc, 0, 0, 0);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
 
-            // ---- softmax: value i of lane (hf, n) is row 8(i/4) + 4 hf + i%4, head n ----
-            const int ebase = st * C::ROWS;
-            f32x16_t &sv = sacc;
-            float mx = -INFINITY;
-            if (ebase + 32 <= nv) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    sv[i] = sacc[i] * p.scale_log2;
-                    mx = fmaxf(mx, sv[i]);
-                }
-            } else {  // last, partial stage: rows past the list end weigh nothing
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int r = 8 * (i >> 2) + 4 * hf + (i & 3);
-                    sv[i] = ebase + r < nv ? sacc[i] * p.scale_log2 : -INFINITY;
-                    mx = fmaxf(mx, sv[i]);
-                }
-            }
-            mx = fmaxf(mx, shfl_xor_f32(mx, 32));
-            m_seen = fmaxf(m_seen, mx);
-            if (__ballot(mx > m_ref + C::SLACK)) {
-                if (__ballot(m_ref > -1e29f) && lane == 0) replay[st & 1] = 1;
-                m_ref = m_seen;
-            }
-            uint32_t pk[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t b = pack_bf16x2(exp2_fast(sv[2 * i] - m_ref), exp2_fast(sv[2 * i + 1] - m_ref));
-                pk[i] = b;
-                l_run += __uint_as_float(b << 16) + __uint_as_float(b & 0xffff0000u);
-            }
-            const bf16x8_t pb0 = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
-            const bf16x8_t pb1 = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[4], pk[5], pk[6], pk[7]});
-
-            // ---- O^T += V^T P^T (operand reads as in the wide kernel) ----
-            {
-                const SA_LDS char *vb = buf + voff;
-                auto vread = [&](int jj) {
-                    const int dt = jj % C::DT, kk = jj / C::DT;
-                    const i16x4_t lo4 = lds_read_tr16(vb + (16 * kk) * C::RS + 64 * dt);
-                    const i16x4_t hi4 = lds_read_tr16(vb + (16 * kk + 8) * C::RS + 64 * dt);
-                    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-                };
-                constexpr int NJ = 2 * C::DT;
-                constexpr int PF = C::PFV;
-                bf16x8_t vq[PF];
-#pragma unroll
-                for (int i = 0; i < PF; ++i) vq[i] = vread(i);
-#pragma unroll
-                for (int jj = 0; jj < NJ; ++jj) {
-                    const bf16x8_t a = vq[jj % PF];
-                    if (jj + PF < NJ) vq[jj % PF] = vread(jj + PF);
-                    acc_o[jj % C::DT] =
-                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, jj >= C::DT ? pb1 : pb0, acc_o[jj % C::DT], 0, 0, 0);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
+            // ---- weights and weighted sum of the stage ----
+            slice_weights_pv<C>(sacc, st * C::ROWS, nv, p.scale_log2, m_ref, m_seen, l_run, have_ref, replay[st & 1],
+                                buf, vlo, vhi, acc_o);
         }
         lds_barrier();  // the last stage's flag is raised by now
         if (replay[0] | replay[1]) {
@@ -926,7 +964,7 @@ __global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const Att
     }
 
     // ---- sink fold + normalise (or f32 partials), stage bf16 rows, store a row per instruction ----
-    l_run += shfl_xor_f32(l_run, 32);  // the head's sum over all rows
+    l_run = sum_xor32(l_run);  // the head's sum over all rows
     asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
     constexpr bool split = SPLIT;  // (a template parameter: the split-free build keeps no partial-store code)
     if (split) {
@@ -958,7 +996,7 @@ __global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const Att
         for (int qd = 0; qd < 4; ++qd) {
             // lane (hf, n) holds head n, d = 32 k + 8 qd + 4 hf + (0..3)
             const f32x16_t &w = acc_o[k];
-            *reinterpret_cast<SA_LDS u32x2_t *>(stg + (wave * 32 + n) * C::RS + 64 * k + 16 * qd + 8 * hf) =
+            *reinterpret_cast<SA_LDS u32x2_t *>(stg + (wave * 32 + n) * C::L::OUT_RS + 64 * k + 16 * qd + 8 * hf) =
                 u32x2_t{pack_bf16x2(w[4 * qd] * inv, w[4 * qd + 1] * inv),
                         pack_bf16x2(w[4 * qd + 2] * inv, w[4 * qd + 3] * inv)};
         }
@@ -974,7 +1012,7 @@ __global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const Att
         u32x4_t v[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            v[i] = *reinterpret_cast<const SA_LDS u32x4_t *>(stg + (r0 + i * C::NW) * C::RS + 16 * lane);
+            v[i] = *reinterpret_cast<const SA_LDS u32x4_t *>(stg + (r0 + i * C::NW) * C::L::OUT_RS + 16 * lane);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int hr = r0 + i * C::NW;
