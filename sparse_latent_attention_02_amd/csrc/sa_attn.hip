@@ -82,6 +82,7 @@ struct AttnParams {
     int32_t n_sp;       // index splits
     int32_t split_len;  // index entries per split
     float scale_log2;   // softmax scale * log2(e)
+    int32_t stagger_cu; // pair kernel: workgroups [stagger_cu, 2 stagger_cu) start late (0: none)
     // fused decode step only: the list is built in the kernel and the step's
     // new latent row is rounded through fp8 and written into its ring slot
     const uint16_t *kv_new;  // [nq][d] this step's raw latent rows
@@ -802,6 +803,17 @@ struct PairCfg {
 template <int D, bool FUSED, bool SPLIT>
 __global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const AttnParams p) {
     using C = PairCfg<D>;
+    // Two workgroups share a CU.  Started together on lists of one length, they
+    // would keep entering their HBM-bound phases (index list and Q in, output
+    // out) at the same moments across the whole chip.  The second round of
+    // workgroups (the CUs' second residency slot) starts a few microseconds
+    // late; every later workgroup takes over the slot of one that ended, so the
+    // two slots of a CU stay apart in phase for the rest of the grid and one
+    // streams while the other computes.  (A bounded wait: two sleeps.)
+    if (p.stagger_cu > 0 && blockIdx.x >= (uint32_t)p.stagger_cu && blockIdx.x < 2u * (uint32_t)p.stagger_cu) {
+        __builtin_amdgcn_s_sleep(100);
+        __builtin_amdgcn_s_sleep(100);
+    }
     __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
     __shared__ int list[C::LIST_CAP];
     __shared__ int wcnt[C::LIST_CAP / 64];
@@ -1652,7 +1664,10 @@ hipError_t launch_wide(const AttnParams &p, hipStream_t stream) {
 }
 
 template <int D, bool FUSED>
-hipError_t launch_pair(const AttnParams &p, hipStream_t stream) {
+hipError_t launch_pair(const AttnParams &p0, hipStream_t stream) {
+    AttnParams p = p0;
+    const int cus = cu_count();
+    p.stagger_cu = p.total_wg >= 2 * cus ? cus : 0;
     if (p.n_sp > 1)
         hipLaunchKernelGGL((sa_attn_pair<D, FUSED, true>), dim3((unsigned)p.total_wg), dim3(PairCfg<D>::THREADS), 0,
                            stream, p);
