@@ -60,9 +60,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kListCap = 4096;        // compacted entries held in LDS at once
 constexpr float kRescaleSlack = 8.0f; // log2 units the reference max may lag behind
-#ifndef SA_PFV_EARLY
-#define SA_PFV_EARLY 1
-#endif
+constexpr int kPfvEarly = 1;          // weighted-sum operand reads issued ahead of the weights (0..2 measured alike)
 
 struct AttnParams {
     const uint16_t *q;
@@ -446,7 +444,7 @@ struct WideCfg {
     static constexpr float SLACK = 32.0f;
     static constexpr int PFK = D > 256 ? 2 : 4;
     static constexpr int PFV = D > 256 ? 2 : 3;
-    static constexpr int PFV_EARLY = SA_PFV_EARLY;  // weighted-sum operand reads issued ahead of the weights
+    static constexpr int PFV_EARLY = kPfvEarly;
     // The next stage's copies are spread evenly over the KS MFMAs of the score
     // product: a wave's memory instructions issue only as fast as the memory
     // pipeline drains, and a wave held up issuing a block of them leaves its MFMA
@@ -792,7 +790,7 @@ struct PairCfg {
     static constexpr float SLACK = 32.0f;
     static constexpr int PFK = D > 256 ? 2 : 4;
     static constexpr int PFV = D > 256 ? 2 : 3;
-    static constexpr int PFV_EARLY = SA_PFV_EARLY;  // weighted-sum operand reads issued ahead of the weights
+    static constexpr int PFV_EARLY = kPfvEarly;
     // the next stage's copies go out over the first quarter of the score product
     // (measured a little faster here than an even spread: two workgroups share
     // the CU's memory pipeline, and the copies start their flight sooner)
