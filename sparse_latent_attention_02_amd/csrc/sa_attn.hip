@@ -135,6 +135,27 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const SA_LDS char *p) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Score product step S^T += K Q^T on MFMA 32x32x16 bf16 with the accumulator
+// in VGPRs.  The compiler picks one register class for the accumulators of all
+// MFMAs of a kernel; with O in the accumulator registers it would put the score
+// tile there too and move an O tile out and back at every stage.  The wait
+// states the hardware does not interlock are placed here: one before each MFMA
+// (a VALU write of a source operand just before), and after the last MFMA of a
+// chain 24 before any VALU reads (or overwrites) the result (8-pass XDL: 11).
+// The first step takes an inline-zero accumulator; the output never shares
+// registers with the operands.
+__device__ __forceinline__ void mfma_s_first(f32x16_t &acc, const bf16x8_t &a, const bf16x8_t &b) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_s_next(f32x16_t &acc, const bf16x8_t &a, const bf16x8_t &b) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_s_last(f32x16_t &acc, const bf16x8_t &a, const bf16x8_t &b) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 15\n\ts_nop 7"
+                 : "+v"(acc)
+                 : "v"(a), "v"(b));
+}
+
 // max / sum of v over lanes l and l ^ 32 (gfx950 v_permlane32_swap: a VALU
 // exchange of the wave's halves, no LDS round trip)
 __device__ __forceinline__ float max_xor32(float v) {
@@ -372,19 +393,26 @@ __device__ __forceinline__ void slice_weights_pv(const f32x16_t &sacc, int ebase
     }
     // exponents t = scale log2(e) s - m_ref (-inf for rows past the list end)
     // and their max, which checks the reference behind the first MFMA below
+    // (two copies of the loop, so full slices carry no masking)
     float mt = -INFINITY;
     uint32_t pk[8];
+    auto weights = [&](auto PARTIAL) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        float t0 = fmaf(sacc[2 * i], scale_log2, -m_ref);
-        float t1 = fmaf(sacc[2 * i + 1], scale_log2, -m_ref);
-        if (partial) {
-            t0 = valid(2 * i) ? t0 : -INFINITY;
-            t1 = valid(2 * i + 1) ? t1 : -INFINITY;
+        for (int i = 0; i < 8; ++i) {
+            float t0 = fmaf(sacc[2 * i], scale_log2, -m_ref);
+            float t1 = fmaf(sacc[2 * i + 1], scale_log2, -m_ref);
+            if constexpr (decltype(PARTIAL)::value) {
+                t0 = valid(2 * i) ? t0 : -INFINITY;
+                t1 = valid(2 * i + 1) ? t1 : -INFINITY;
+            }
+            mt = fmaxf(mt, fmaxf(t0, t1));
+            pk[i] = pack_bf16x2(exp2_fast(t0), exp2_fast(t1));
         }
-        mt = fmaxf(mt, fmaxf(t0, t1));
-        pk[i] = pack_bf16x2(exp2_fast(t0), exp2_fast(t1));
-    }
+    };
+    if (partial)
+        weights(std::true_type{});
+    else
+        weights(std::false_type{});
     const bf16x8_t pb0 = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
     const bf16x8_t pb1 = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[4], pk[5], pk[6], pk[7]});
 #pragma unroll
@@ -619,7 +647,7 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
             //      Operand reads run four MFMAs ahead; the next stage's copies go out one
             //      or a few per k-step, so the wave is not held up issuing them in a block;
             //      the scheduling barriers keep the compiler from hoisting the reads ----
-            f32x16_t sacc = {};
+            f32x16_t sacc;
             {
                 constexpr int PF = C::PFK;
                 bf16x8_t kq[PF];
@@ -630,7 +658,12 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
                     const bf16x8_t a = kq[ks % PF];
                     if (ks + PF < C::KS) kq[ks % PF] = lds_read_b128(buf + C::L::koff(kb, ks + PF));
                     if (more) copy_rows(st + 1, rows_next, C::copy_at(ks), C::copy_at(ks + 1));
-                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc, 0, 0, 0);
+                    if (ks == 0)
+                        mfma_s_first(sacc, a, qreg[ks]);
+                    else if (ks + 1 < C::KS)
+                        mfma_s_next(sacc, a, qreg[ks]);
+                    else
+                        mfma_s_last(sacc, a, qreg[ks]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -938,7 +971,7 @@ __global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const Att
             const int rows_next = more ? stage_rows(st + 1) : 0;
 
             // ---- scores S^T[32 rows][32 heads]; the next stage's copies spread over them ----
-            f32x16_t sacc = {};
+            f32x16_t sacc;
             {
                 constexpr int PF = C::PFK;
                 bf16x8_t kq[PF];
@@ -949,7 +982,12 @@ __global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const Att
                     const bf16x8_t a = kq[ks % PF];
                     if (ks + PF < C::KS) kq[ks % PF] = lds_read_b128(buf + C::L::koff(kb, ks + PF));
                     if (more) copy_rows(st + 1, rows_next, C::copy_at(ks), C::copy_at(ks + 1));
-                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc, 0, 0, 0);
+                    if (ks == 0)
+                        mfma_s_first(sacc, a, qreg[ks]);
+                    else if (ks + 1 < C::KS)
+                        mfma_s_next(sacc, a, qreg[ks]);
+                    else
+                        mfma_s_last(sacc, a, qreg[ks]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
