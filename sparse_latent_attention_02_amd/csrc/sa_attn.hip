@@ -293,6 +293,16 @@ struct Compactor {
         }
     }
 
+    // the raw entries of [c0, c1) from list[] (placed there by direct copies:
+    // entry e at list[e - c0]); read before pack() rewrites list[]
+    __device__ __forceinline__ void load_lds(const int *list, int c0, int c1) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int e = c0 + k * NT + (int)threadIdx.x;
+            v[k] = e < c1 ? list[e - c0] : -1;
+        }
+    }
+
     // wait for the entry loads here: a compiler-placed wait for them further on
     // would also wait for every copy queued behind them
     __device__ __forceinline__ void ready() const {
@@ -872,15 +882,31 @@ __global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const Att
     u32x4_t new_raw = {0u, 0u, 0u, 0u};
     if (has_new && wave == 0 && chunk_lane)
         new_raw = *reinterpret_cast<const u32x4_t *>(p.kv_new + (int64_t)qi * D + lane * 8);
-    // the first index chunk goes in flight before anything else: it heads the critical path
+    // Index entries, the head of the critical path.  The fused step builds them in
+    // place.  Otherwise a chunk's raw entries are copied global -> list[]
+    // directly (4 bytes a lane, 64 entries a wave instruction, entry e at
+    // list[e - c0]): Q's copies then go out right behind them, and the wait for
+    // the entries (vmcnt counts completions in issue order) leaves Q in flight --
+    // the two memory round trips overlap instead of following each other.
     Compactor<C::THREADS, C::LIST_CAP> cmp;
-    cmp.load(fetch, lo, min(hi, lo + C::LIST_CAP));
+    const uint32_t list_base = lds_addr((const SA_LDS void *)list);
+    auto copy_idx = [&](int c0, int c1) {
+#pragma unroll 1
+        for (int e0 = c0 + wave * 64; e0 < c1; e0 += C::THREADS)
+            if (e0 + lane < c1) dma_4B(idxq + e0 + lane, list_base + (uint32_t)(e0 - c0) * 4);
+    };
+    if (FUSED)
+        cmp.load(fetch, lo, min(hi, lo + C::LIST_CAP));
+    else
+        copy_idx(lo, min(hi, lo + C::LIST_CAP));
     const int head = ((int)hg * 2 + wave) * 32 + n;
     const bool head_ok = head < p.h;
-    // the head's sink, ahead of any copy (a load issued behind the copies waits for them)
+    // the head's sink, ahead of Q's copies (a load issued behind the copies waits for them)
     const float sink_any = p.sink[min(head, p.h - 1)];
 
-    cmp.ready();
+    if (FUSED) cmp.ready();
+    const bool rot = p.rope != nullptr && p.n_sp == 1;
+    if (rot && wave == 0) copy_rope_row(p, qi, lane, lds_addr((const SA_LDS void *)rtab));
     // Q rows: wave w copies its own 32 head rows (one 1 KiB row per wave
     // instruction) into rows 32 w .. 32 w + 31 of the stage buffers, to be read
     // into registers once the list is packed; a head past h takes row 0 of the
@@ -900,9 +926,6 @@ __global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const Att
             *reinterpret_cast<u32x4_t *>(p.kv_ring + ((int64_t)bi * p.rows + p.new_slot) * D + lane * 8) = r;
         asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
     }
-
-    const bool rot = p.rope != nullptr && p.n_sp == 1;
-    if (rot && wave == 0) copy_rope_row(p, qi, lane, lds_addr((const SA_LDS void *)rtab));
     const SA_LDS char *lds = (const SA_LDS char *)smem;
 
     float m_ref = -1e30f;
@@ -928,7 +951,22 @@ __global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const Att
     again = false;
     for (int c0 = lo; c0 < hi; c0 += C::LIST_CAP) {
         const int c1 = min(hi, c0 + C::LIST_CAP);
-        if (c0 != lo || !first_pass) cmp.load(fetch, c0, c1);
+        if (c0 != lo || !first_pass) {
+            if (FUSED)
+                cmp.load(fetch, c0, c1);
+            else
+                copy_idx(c0, c1);
+        }
+        if (!FUSED) {
+            // this wave's entry copies are in (on the first chunk Q's 32 copies,
+            // issued behind them, may still fly); then everyone's
+            if (c0 == lo && first_pass)
+                asm volatile("s_waitcnt vmcnt(32)" : : : "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+            lds_barrier();
+            cmp.load_lds(list, c0, c1);
+        }
         if (FUSED && first_pass && hg == 0 && p.idx_out) cmp.store(p.idx_out + (int64_t)qi * p.topk, c0, c1);
         const int nv = cmp.pack(p.rows, list, wcnt);
         const int nst = (nv + C::ROWS - 1) / C::ROWS;

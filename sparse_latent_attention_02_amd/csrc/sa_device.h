@@ -63,6 +63,16 @@ __device__ __forceinline__ void dma_16B(const void *src, uint32_t lds_base) {
                  : "memory", "m0");
 }
 
+// Direct global -> LDS copy of one 4-byte value per lane (gfx950
+// global_load_lds_dword): lane i's value lands at lds_base + 4 i (inactive lanes
+// write nothing).  Completion is tracked by the caller's vmcnt waits.
+__device__ __forceinline__ void dma_4B(const void *src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(src), "s"(lds_base)
+                 : "memory", "m0");
+}
+
 // Wait until at most N vector-memory operations of this wave are outstanding,
 // then barrier the workgroup (all LDS writes of completed copies visible).
 template <int N>
