@@ -809,11 +809,13 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
 // softmax against the fixed reference of the wide kernel, O^T[d][32 heads] +=
 // V^T P^T, all on MFMA 32x32x16 with the operand layouts of the wide kernel.
 // A wavefront thus ends with its heads' whole result: no merge between
-// wavefronts.  With 32-row stages and a 2048-entry list chunk the workgroup
-// needs under 80 KiB of LDS, so two workgroups share a CU and the prologue
-// (list compaction, Q loads) and epilogue (normalisation, stores) of one
-// overlap the stages of the other.
-template <int D>
+// wavefronts.  With 32-row stages and a list chunk of up to 2176 entries the
+// workgroup needs under 80 KiB of LDS, so two workgroups share a CU and the
+// prologue (list compaction, Q loads) and epilogue (normalisation, stores) of
+// one overlap the stages of the other.  The chunk capacity is a template
+// parameter (the compaction's work grows with it): 512 for short lists, 2176
+// for long ones (a 128 + 2048-entry list in one pass).
+template <int D, int LCAP>
 struct PairCfg {
     static constexpr int NW = 2;
     static constexpr int THREADS = 64 * NW;
@@ -827,9 +829,10 @@ struct PairCfg {
     static constexpr int DT = D / 32;
     static constexpr int STAGE_BYTES = ROWS * RS;
     static constexpr int NBUF = 2;
-    static constexpr int LIST_CAP = 2048;       // compacted entries held at once
+    static constexpr int LIST_CAP = LCAP;       // compacted entries held at once
     static constexpr int OUT_BYTES = HEADS * L::OUT_RS;  // staged bf16 output, over the stage buffers
     static constexpr int SMEM = std::max(NBUF * STAGE_BYTES, OUT_BYTES);
+    static_assert(SMEM - OUT_BYTES >= 4 * D, "room for the rotation table row past the staged output");
     static constexpr float SLACK = 32.0f;
     static constexpr int PFK = D > 256 ? 2 : 4;
     static constexpr int PFV = D > 256 ? 2 : 3;
@@ -841,9 +844,10 @@ struct PairCfg {
     static_assert(KS >= 4 && DT >= 2 && RPW == 16, "tiling");
 };
 
-template <int D, bool FUSED, bool SPLIT>
-__global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const AttnParams p) {
-    using C = PairCfg<D>;
+template <int D, int LCAP, bool FUSED, bool SPLIT>
+__global__ void __launch_bounds__(128, 2) sa_attn_pair(const AttnParams p) {
+    using C = PairCfg<D, LCAP>;
+    static_assert(C::THREADS == 128, "launch bounds");
     // Two workgroups share a CU.  Started together on lists of one length, they
     // would keep entering their HBM-bound phases (index list and Q in, output
     // out) at the same moments across the whole chip.  The second round of
@@ -859,7 +863,6 @@ __global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const Att
     __shared__ int list[C::LIST_CAP];
     __shared__ int wcnt[C::LIST_CAP / 64];
     __shared__ int replay[2];
-    __shared__ __attribute__((aligned(16))) float rtab[D];  // the query's rotation table row
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // head tile
@@ -905,8 +908,10 @@ __global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const Att
     const float sink_any = p.sink[min(head, p.h - 1)];
 
     if (FUSED) cmp.ready();
+    // the output's inverse rotation: the query's table row is copied in the
+    // epilogue, past the staged output rows (the stage buffers hold Q and rows
+    // until then; no LDS of its own, which leaves room for a 2304-entry list)
     const bool rot = p.rope != nullptr && p.n_sp == 1;
-    if (rot && wave == 0) copy_rope_row(p, qi, lane, lds_addr((const SA_LDS void *)rtab));
     // Q rows: wave w copies its own 32 head rows (one 1 KiB row per wave
     // instruction) into rows 32 w .. 32 w + 31 of the stage buffers, to be read
     // into registers once the list is packed; a head past h takes row 0 of the
@@ -1076,6 +1081,8 @@ __global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const Att
     const float inv = Lt > 0.f ? 1.0f / Lt : 0.f;
     lds_barrier();  // stage buffers free
     SA_LDS char *stg = (SA_LDS char *)smem;
+    const SA_LDS float *rtab = (const SA_LDS float *)(stg + C::OUT_BYTES);
+    if (rot && wave == 0) copy_rope_row(p, qi, lane, smem_base + (uint32_t)C::OUT_BYTES);
 #pragma unroll
     for (int k = 0; k < C::DT; ++k) {
 #pragma unroll
@@ -1090,6 +1097,7 @@ __global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const Att
         // ahead would need as many vector registers again and spill
         __builtin_amdgcn_sched_barrier(0);
     }
+    if (rot && wave == 0) asm volatile("s_waitcnt vmcnt(0)" : : : "memory");  // the table row is in
     lds_barrier();
     // one head row per wave instruction (lane l: chunk l), in batches of 8 rows
     // whose LDS reads all go out before their stores
@@ -1105,7 +1113,7 @@ __global__ void __launch_bounds__(PairCfg<D>::THREADS, 2) sa_attn_pair(const Att
             const int hglob = (int)hg * C::HEADS + hr;
             if (hglob < p.h && chunk_lane) {
                 u32x4_t w = v[i];
-                if (rot) w = unrotate_chunk(w, 8 * lane, D, p.rope_dim, (const SA_LDS float *)rtab);
+                if (rot) w = unrotate_chunk(w, 8 * lane, D, p.rope_dim, rtab);
                 *reinterpret_cast<u32x4_t *>(p.out + ((int64_t)qi * p.h + hglob) * D + lane * 8) = w;
             }
         }
@@ -1687,6 +1695,8 @@ void set_splits(Variant &v, int32_t topk, int n_sp) {
 // enough to share.
 constexpr int kDecodeMaxTopk = 512;
 constexpr int kPairMinPerCu = 4;
+constexpr int kPairShortList = 512;   // pair kernel list chunk for lists up to this many entries
+constexpr int kPairLongList = 2176;   // and for longer ones (a 128 + 2048-entry list in one pass)
 
 Variant choose_variant(int64_t nq, int32_t h, int32_t topk, int cus) {
     Variant v{SA_KERNEL_WIDE, 64, 1, std::max(topk, 1)};
@@ -1742,12 +1752,23 @@ hipError_t launch_pair(const AttnParams &p0, hipStream_t stream) {
     AttnParams p = p0;
     const int cus = cu_count();
     p.stagger_cu = p.total_wg >= 2 * cus ? cus : 0;
-    if (p.n_sp > 1)
-        hipLaunchKernelGGL((sa_attn_pair<D, FUSED, true>), dim3((unsigned)p.total_wg), dim3(PairCfg<D>::THREADS), 0,
-                           stream, p);
-    else
-        hipLaunchKernelGGL((sa_attn_pair<D, FUSED, false>), dim3((unsigned)p.total_wg), dim3(PairCfg<D>::THREADS), 0,
-                           stream, p);
+    // list chunk capacity: the entries one workgroup handles, rounded up
+    const int per_wg = std::min(p.topk, p.split_len);
+    if (per_wg <= kPairShortList) {
+        if (p.n_sp > 1)
+            hipLaunchKernelGGL((sa_attn_pair<D, kPairShortList, FUSED, true>), dim3((unsigned)p.total_wg), dim3(128),
+                               0, stream, p);
+        else
+            hipLaunchKernelGGL((sa_attn_pair<D, kPairShortList, FUSED, false>), dim3((unsigned)p.total_wg),
+                               dim3(128), 0, stream, p);
+    } else {
+        if (p.n_sp > 1)
+            hipLaunchKernelGGL((sa_attn_pair<D, kPairLongList, FUSED, true>), dim3((unsigned)p.total_wg), dim3(128),
+                               0, stream, p);
+        else
+            hipLaunchKernelGGL((sa_attn_pair<D, kPairLongList, FUSED, false>), dim3((unsigned)p.total_wg),
+                               dim3(128), 0, stream, p);
+    }
     return hipGetLastError();
 }
 
