@@ -480,7 +480,7 @@ struct WideCfg {
     // d = 512 Q and O fill the register file and the depth is kept small
     // log2 units a stage max may exceed the fixed reference of the weights
     static constexpr float SLACK = 32.0f;
-    static constexpr int PFK = D > 256 ? 2 : 4;
+    static constexpr int PFK = D > 256 ? 3 : 4;
     static constexpr int PFV = D > 256 ? 2 : 3;
     static constexpr int PFV_EARLY = kPfvEarly;
     // The next stage's copies are spread evenly over the KS MFMAs of the score
@@ -834,7 +834,7 @@ struct PairCfg {
     static constexpr int SMEM = std::max(NBUF * STAGE_BYTES, OUT_BYTES);
     static_assert(SMEM - OUT_BYTES >= 4 * D, "room for the rotation table row past the staged output");
     static constexpr float SLACK = 32.0f;
-    static constexpr int PFK = D > 256 ? 2 : 4;
+    static constexpr int PFK = D > 256 ? 3 : 4;
     static constexpr int PFV = D > 256 ? 2 : 3;
     static constexpr int PFV_EARLY = kPfvEarly;
     // the next stage's copies go out over the first quarter of the score product
