@@ -109,6 +109,10 @@ SMALL = [
     (11, 2, 1, 64, 64, 6000, 5000, 0.1),   # longer than one compaction chunk
     (12, 1, 1, 16, 128, 80, 70, 0.1),
     (13, 1, 1, 16, 256, 80, 70, 0.1),
+    (14, 1, 2, 64, 512, 1000, 512, 0.2),    # the pair kernel's short-list chunk, full
+    (15, 2, 2, 64, 512, 1000, 513, 0.2),    # ... one entry past it: the long-list chunk
+    (16, 1, 2, 64, 512, 3000, 2176, 0.1),   # a 128 + 2048-entry list in one chunk
+    (17, 1, 2, 64, 512, 5000, 2177, 0.0),   # one entry past it: two chunks
 ]
 VARIANTS = [None, (1, 1), (1, 2), (1, 3), (1, 7), (2, 1), (2, 2), (2, 5), (3, 1), (3, 2), (3, 5)]
 

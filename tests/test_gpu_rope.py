@@ -84,6 +84,7 @@ ATTN_CASES = [
     (14, 1, 5, 8, 64, 40, 16, 64, 2),           # the whole row rotated
     (15, 1, 3, 16, 512, 64, 64, 512, 0),        # a table row of two copy instructions
     (16, 2, 2, 16, 512, 64, 50, 264, 3),        # ... the second one partial
+    (17, 1, 3, 64, 512, 3000, 1500, 64, 100),   # a long list (the pair kernel's long-list chunk)
 ]
 VARIANTS = [None, (1, 1), (1, 3), (2, 1), (2, 4), (3, 1), (3, 3)]
 
