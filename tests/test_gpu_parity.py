@@ -151,6 +151,48 @@ def test_sparse_attn_scores_outrunning_the_first_stage(d, variant):
     assert np.allclose(r, kv[:, 250].float().numpy(), rtol=2e-2, atol=2e-2)
 
 
+@pytest.mark.parametrize("d", [64, 128, 512])
+@pytest.mark.parametrize("topk", [64, 130])
+@pytest.mark.parametrize("variant", [None, (1, 1), (1, 2), (2, 1), (2, 2), (3, 1), (3, 2)],
+                         ids=lambda v: "auto" if v is None else "k%d_sp%d" % v)
+def test_sparse_attn_one_hot_rows_and_heads(d, topk, variant):
+    """Row i of the cache is (1 + i // d) at dim i % d and 0 elsewhere; each (query,
+    head) has one nonzero query value, at a dim of its own.  Every row then lands at a
+    known dim of the output with a known weight, so a row or a head-row chunk copied to
+    the wrong place, or read by the wrong wavefront, changes the output exactly where
+    it shows.  Three launches in a row must agree bit for bit."""
+    b, s, h = 1, 2, 32
+    rows = max(topk, d)
+    kv = torch.zeros((b, rows, d))
+    for i in range(rows):
+        kv[0, i, i % d] = 1.0 + i // d
+    q = torch.zeros((b, s, h, d))
+    for qi in range(s):
+        for hh in range(h):
+            q[0, qi, hh, (7 * hh + qi) % d] = 2.0
+    kv, q = kv.to(torch.bfloat16), q.to(torch.bfloat16)
+    sink = torch.full((h,), -30.0)
+    idx = torch.arange(topk, dtype=torch.int32).view(1, 1, topk).repeat(b, s, 1).contiguous()
+    got, ref = run_both(dict(q=q, kv=kv, sink=sink, idx=idx), variant, scale=1.0)
+    # the closed form: softmax over the rows (the sink adds e^-30 to the denominator)
+    ii = np.arange(topk)
+    val = 1.0 + ii // d
+    want = np.zeros((s, h, d))
+    for qi in range(s):
+        for hh in range(h):
+            j = (7 * hh + qi) % d
+            sc = np.where(ii % d == j, 2.0 * val, 0.0)
+            w = np.exp(sc - sc.max())
+            w /= w.sum() + np.exp(-30.0 - sc.max())
+            np.add.at(want[qi, hh], ii % d, w * val)
+    assert np.allclose(ref.reshape(s, h, d), want, rtol=1e-5, atol=1e-6)
+    assert_parity(got, ref, f"one-hot d {d} topk {topk} variant {variant}")
+    for _ in range(2):
+        again = sa.sparse_attn(to_dev(q), to_dev(kv), to_dev(sink), to_dev(idx), 1.0, variant=variant)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(again), got)
+
+
 def test_sparse_attn_edge_cases():
     # all -1, topk 0, sink -inf, invalid entries
     c = wl.small_case(21, 2, 3, 16, 512, 40, 40, 0.0)
