@@ -13,10 +13,14 @@ from about half the gathered bytes.  ``--rope`` fuses the output's inverse
 rotary embedding into the epilogue.  ``--select`` measures the indexer's
 selection tail on its own workload instead (one JSON line of its own).
 
-Default workload: decode over the window ring, batch 64 single-query steps at
-position 5000, 64 heads, head dim 512, 128-slot ring (the configuration the
-metric is quoted on).  ``--workload N`` measures the other configurations the
-same way (1 = tiny ring run is correctness-only and not benchmarked).
+Default workload: the long prefill with compressed positions -- 8192 queries,
+64 heads, head dim 512, each query's list a causal 128-wide window plus up to
+2048 compressed positions (1.24 TFLOP of attention per step, MFMA bound): the
+largest configuration, and the one whose whole work a step covers on one GPU.
+``--workload N`` measures the other configurations the same way: 2 = decode over
+the window ring (batch 64 at position 5000, HBM bound), 3 = window-only prefill
+(4096 queries), 4 = decode with compressed positions (batch 128, 128 heads);
+1 = the tiny ring run is correctness-only and not benchmarked.
 
 Inputs are resident in HBM before the timed region.  Small workloads rotate
 through enough independently generated input sets (more than twice the 256 MiB
@@ -53,7 +57,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=5, choices=[2, 3, 4, 5])
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")

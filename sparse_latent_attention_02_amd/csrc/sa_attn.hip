@@ -24,9 +24,10 @@
 //     and no traffic;
 //  2. gather: stages of rows copied HBM -> LDS with the direct global->LDS path
 //     (16 B per lane, one 1 KiB row per wave instruction at d = 512), two
-//     buffers, so the copy of stage t+1 overlaps the maths of stage t.  LDS rows
-//     are padded by 48 bytes, which keeps the score operand reads free of bank
-//     conflicts and makes every operand address a per-lane base plus an
+//     buffers, so the copy of stage t+1 overlaps the maths of stage t.  A row
+//     takes 2 d + 64 bytes of LDS with its 16-byte chunks swizzled in groups of
+//     four rows (RowLayout below), which keeps both operand read patterns free
+//     of bank conflicts and makes every operand address a per-lane base plus an
 //     immediate;
 //  3. scores S^T[32 rows][32 heads] = K[rows][:] . Q[heads][:]^T on MFMA
 //     32x32x16 bf16 (A = gathered rows from LDS, B = the wave's Q held in

@@ -56,8 +56,14 @@ __device__ __forceinline__ uint32_t lds_addr(const SA_LDS void *p) {
 // wave-uniform LDS byte address `lds_base` (lane i at lds_base + 16 i).  Issued
 // through inline asm so that the compiler adds no waits of its own; completion
 // is tracked by the caller with wait_vmcnt_barrier().
+//
+// The copy takes its LDS address from M0.  On gfx950 an LDS DMA that follows
+// an SALU write of M0 with no wait state in between can read the previous M0
+// (the compiler puts an s_nop 0 there for its own global_load_lds), which
+// would land the row in the previous copy's slot; the asm keeps that wait
+// state itself, since the compiler cannot see into it.
 __device__ __forceinline__ void dma_16B(const void *src, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :
                  : "v"(src), "s"(lds_base)
                  : "memory", "m0");
@@ -65,9 +71,10 @@ __device__ __forceinline__ void dma_16B(const void *src, uint32_t lds_base) {
 
 // Direct global -> LDS copy of one 4-byte value per lane (gfx950
 // global_load_lds_dword): lane i's value lands at lds_base + 4 i (inactive lanes
-// write nothing).  Completion is tracked by the caller's vmcnt waits.
+// write nothing).  Completion is tracked by the caller's vmcnt waits; the
+// M0 wait state as in dma_16B.
 __device__ __forceinline__ void dma_4B(const void *src, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                  :
                  : "v"(src), "s"(lds_base)
                  : "memory", "m0");

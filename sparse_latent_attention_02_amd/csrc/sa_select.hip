@@ -28,9 +28,13 @@ constexpr int kPerThread = 16;  // consecutive positions per thread in the order
 constexpr int kMaxBins = 4096;  // the widest digit: 12 bits
 
 // f32 -> u32 with the same order (larger value, larger key); -inf is the
-// smallest non-NaN key, and a masked position takes that key.
+// smallest non-NaN key, and a masked position takes that key.  -0.0 and +0.0
+// compare equal as scores, so -0.0 takes +0.0's key: equal scores then fall to
+// the lower position, as for any other tie (a ReLU score times a negative
+// weight gives -0.0).
 __device__ __forceinline__ uint32_t order_key(float x) {
-    const uint32_t u = __float_as_uint(x);
+    uint32_t u = __float_as_uint(x);
+    if (u == 0x80000000u) u = 0u;
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 constexpr uint32_t kKeyNegInf = 0x007fffffu;  // order_key(-inf)

@@ -1,8 +1,9 @@
 """GPU parity of the indexer's selection tail (sa_indexer_topk): bit for bit
 against the oracle (both take equal scores at the lower position first), on
 decode rows short enough for LDS and longer ones, causal prefill masks, the
-take-everything case, heavy ties, -inf scores, and writes into the compressed
-columns of a wider index buffer (other columns untouched)."""
+take-everything case, heavy ties, -inf scores, zeros of both signs straddling
+the k-th score (equal scores: -0.0 and +0.0 rank alike), and writes into the
+compressed columns of a wider index buffer (other columns untouched)."""
 import numpy as np
 import pytest
 import torch
@@ -32,6 +33,10 @@ CASES = [
     (6, 4, 1, 20000, 4, 300, 0, "neginf"),         # -inf scores among finite ones
     (7, 3, 5, 77, 3, 9, 17, "normal"),             # a chunk after position 0
     (8, 2, 1, 4095, 1, 4096, 5, "ties"),           # ratio 1, topk = T
+    (9, 16, 1, 16383, 4, 1000, 128, "zeros"),      # decode: +0 and -0 on both sides of the k-th score
+    (10, 1, 2048, 0, 4, 200, 2048, "zeros"),       # prefill: the same, under the causal mask
+    (11, 8, 1, 65535, 4, 2048, 128, "relu"),       # decode: ReLU scores times signed weights (many -0)
+    (12, 2, 1, 131071, 4, 2048, 128, "zeros"),     # decode: rows re-read from memory, signed zeros
 ]
 
 
@@ -39,6 +44,17 @@ def make_scores(seed, b, s, T, kind):
     g = torch.Generator().manual_seed(seed)
     if kind == "ties":
         return torch.randint(0, 4, (b, s, T), generator=g).to(torch.float32)
+    if kind == "zeros":
+        # 10% +1, 10% -1, the rest zeros of random sign: the k-th largest score
+        # is a zero, with +0 and -0 entries on both sides of the cut
+        u = torch.rand((b, s, T), generator=g)
+        sign = torch.where(torch.rand((b, s, T), generator=g) < 0.5, -1.0, 1.0)
+        return torch.where(u < 0.1, 1.0, torch.where(u < 0.2, -1.0, 0.0 * sign)).to(torch.float32)
+    if kind == "relu":
+        # the indexer's score form: ReLU of a logit times a signed weight
+        x = torch.relu(torch.randn((b, s, T), generator=g))
+        wgt = torch.randn((b, s, T), generator=g)
+        return (x * wgt).to(torch.float32)
     sc = torch.randn((b, s, T), generator=g)
     if kind == "neginf":
         sc[torch.rand((b, s, T), generator=g) < 0.3] = -torch.inf
@@ -51,6 +67,9 @@ def test_indexer_topk_vs_oracle(case):
     T = (start_pos + s) // ratio
     print(f"indexer tail case {case} T={T}", flush=True)
     sc = make_scores(seed, b, s, T, kind)
+    if kind in ("zeros", "relu"):
+        z = sc == 0
+        assert bool((z & torch.signbit(sc)).any()) and bool((z & ~torch.signbit(sc)).any())
     ref = oracle.indexer_topk(sc.numpy(), start_pos, ratio, index_topk, offset)
     got = sa.indexer_topk(sc.to(DEV), start_pos, ratio, index_topk, offset)
     torch.cuda.synchronize()

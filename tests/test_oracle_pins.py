@@ -669,6 +669,29 @@ def test_indexer_tail_ties_take_the_lower_position(oracle_lib):
     assert 5 not in oracle.indexer_topk(sc, 159, 4, 39, 0)[0, 0]
 
 
+def test_indexer_tail_signed_zeros_are_one_score(oracle_lib):
+    """-0.0 and +0.0 are equal scores (IEEE comparison; a ReLU score times a
+    negative weight gives -0.0), so among zeros of either sign the lower
+    position wins, as for any tie.  Checked against a numpy ranking by
+    (score descending, position ascending) with numpy's own comparisons."""
+    sc = np.full((1, 1, 40), -1.0, dtype=np.float32)
+    sc[0, 0, 0], sc[0, 0, 1] = -0.0, 0.0
+    assert np.array_equal(oracle.indexer_topk(sc, 159, 4, 1, 0)[0, 0], [0])      # -0 at the lower position
+    sc[0, 0, 0], sc[0, 0, 1] = 0.0, -0.0
+    assert np.array_equal(oracle.indexer_topk(sc, 159, 4, 1, 0)[0, 0], [0])
+    g = np.random.default_rng(7)
+    for trial in range(20):
+        T = 300
+        relu = np.maximum(g.standard_normal(T), 0.0) * (g.random(T) < 0.3)        # mostly exact zeros
+        w = np.where(g.random(T) < 0.5, -1.0, 1.0) * g.random(T)
+        scores = (relu * w).astype(np.float32)                                    # +0, -0, and signed values
+        assert np.signbit(scores[scores == 0]).any() and (~np.signbit(scores[scores == 0])).any()
+        k = int(g.integers(1, T))
+        got = oracle.indexer_topk(scores.reshape(1, 1, T), 4 * T - 1, 4, k, 3)[0, 0]
+        order = np.lexsort((np.arange(T), -scores.astype(np.float64)))
+        assert np.array_equal(got, np.sort(order[:k]) + 3), trial
+
+
 def test_indexer_tail_rejects_bad_shapes(oracle_lib):
     sc = np.zeros((1, 1, 10), dtype=np.float32)
     with pytest.raises(oracle.OracleError) as e:
