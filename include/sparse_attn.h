@@ -236,6 +236,34 @@ sa_status sa_sparse_attn_ex(const uint16_t *q, const uint16_t *kv, const float *
                             int32_t kernel, int32_t splits);
 
 /* ------------------------------------------------------------------------
+ * sa_sparse_attn_ex with no workspace argument and no allocation -- for callers
+ * that cannot allocate device memory at the call (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid it).
+ *
+ * Same arguments, variant choice and result (bit for bit) as sa_sparse_attn_ex
+ * with kernel and splits as given.  When the variant splits the index list, its
+ * f32 partials go to a scratch array of the library's own in device memory,
+ * sa_sparse_attn_noalloc_scratch_bytes() (32 MiB) on each device the library
+ * runs on, held until the process ends.  A call whose partials need more
+ * (sa_sparse_attn_workspace_bytes_ex(b, s, h, d, topk, kernel, splits) above
+ * that) returns SA_ERR_SHAPE with nothing enqueued; a call that needs none
+ * does not touch the array.  The call makes no hipMalloc, hipFree or other
+ * allocating call; the first call on a device looks up the array's address
+ * there (SA_ERR_HIP if that fails).
+ *
+ * Every call on one device shares that device's array, and the kernels of a
+ * call use it until they finish: calls whose work overlaps on one device
+ * (different streams, or host threads without ordering between their streams)
+ * race on it and must be serialised by the caller.  Nothing in the array needs
+ * to start at zero; each call writes every partial it reads. */
+size_t sa_sparse_attn_noalloc_scratch_bytes(void);
+
+sa_status sa_sparse_attn_noalloc(const uint16_t *q, const uint16_t *kv, const float *sink,
+                                 const int32_t *idx, int64_t b, int64_t s, int32_t h, int32_t d,
+                                 int64_t rows, int32_t topk, float scale, uint16_t *out, void *stream,
+                                 int32_t kernel, int32_t splits);
+
+/* ------------------------------------------------------------------------
  * One decode step in one launch -- [QLAT] Attention.forward at a decode step
  * (the new KV row rounded through fp8 and written into the ring, the window
  * list, the compressed indices concatenated after it, sparse_attn), [ATTEND]

@@ -11,6 +11,7 @@ Names follow the C ABI:
   act_quant_fp8_                           -- fp8 (e4m3) round trip of bf16 rows, in place
   window_kv_update                         -- fp8 round trip of new rows + ring-cache write
   sparse_attn                              -- the attention itself
+  sparse_attn_noalloc                      -- the same with no workspace argument, allocating nothing
   sparse_attn_decode_step                  -- a whole decode step (ring write, lists, attention) in one launch
   kv8_pack / kv8_unpack                    -- fp8-resident KV rows (e4m3fn codes + E8M0 block scales)
   sparse_attn_kv8 / sparse_attn_decode_step_kv8 -- the attention and the decode step over kv8 rows
@@ -82,11 +83,14 @@ def lib() -> ctypes.CDLL:
         L.sa_sparse_attn_decode_step_rope.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i64, i32, i32, i64,
                                                       f32, vp, vp, sz, vp, i32, i32, vp, i64, i32]
         L.sa_indexer_topk.argtypes = [vp, i64, i64, i32, i64, i32, i32, i32, vp, i64, i32, vp]
+        L.sa_sparse_attn_noalloc_scratch_bytes.argtypes = []
+        L.sa_sparse_attn_noalloc_scratch_bytes.restype = sz
+        L.sa_sparse_attn_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i64, i32, f32, vp, vp, i32, i32]
         for fn in ("sa_window_topk_idxs_shape", "sa_window_topk_idxs", "sa_append_compressed_idxs",
                    "sa_act_quant_fp8_inplace", "sa_window_kv_update", "sa_sparse_attn", "sa_sparse_attn_ex",
                    "sa_sparse_attn_decode_step", "sa_kv8_pack", "sa_kv8_unpack", "sa_sparse_attn_kv8",
                    "sa_sparse_attn_decode_step_kv8", "sa_apply_rotary", "sa_sparse_attn_rope",
-                   "sa_sparse_attn_decode_step_rope", "sa_indexer_topk"):
+                   "sa_sparse_attn_decode_step_rope", "sa_indexer_topk", "sa_sparse_attn_noalloc"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -221,6 +225,37 @@ def sparse_attn(q: torch.Tensor, kv: torch.Tensor, sink: torch.Tensor, idx: torc
         _check("sa_sparse_attn", lib().sa_sparse_attn(*args))
     else:
         _check("sa_sparse_attn_ex", lib().sa_sparse_attn_ex(*args, *variant))
+    return out
+
+
+def noalloc_scratch_bytes() -> int:
+    """Size of the library's own per-device scratch used by sparse_attn_noalloc."""
+    return int(lib().sa_sparse_attn_noalloc_scratch_bytes())
+
+
+def sparse_attn_noalloc(q: torch.Tensor, kv: torch.Tensor, sink: torch.Tensor, idx: torch.Tensor, scale: float,
+                        out: torch.Tensor, variant: tuple | None = None, stream=None) -> torch.Tensor:
+    """sparse_attn with no workspace argument: the library allocates nothing and
+    keeps split partials in its own per-device scratch (sa_sparse_attn_noalloc).
+    ``out`` is required (the call allocates nothing).  Calls whose work overlaps
+    on one device race on the scratch."""
+    _dev(q, "q", torch.bfloat16)
+    _dev(kv, "kv", torch.bfloat16)
+    _dev(sink, "sink", torch.float32)
+    _dev(idx, "idx", torch.int32)
+    _dev(out, "out", torch.bfloat16)
+    b, s, h, d = q.shape
+    if kv.dim() != 3 or kv.shape[0] != b or kv.shape[2] != d:
+        raise ValueError(f"kv must be [{b}][rows][{d}], got {tuple(kv.shape)}")
+    if idx.dim() != 3 or idx.shape[0] != b or idx.shape[1] != s:
+        raise ValueError(f"idx must be [{b}][{s}][topk], got {tuple(idx.shape)}")
+    if sink.shape != (h,) or out.shape != q.shape:
+        raise ValueError("sink must be [h] and out shaped like q")
+    k, sp = variant if variant is not None else (0, 0)
+    _check("sa_sparse_attn_noalloc",
+           lib().sa_sparse_attn_noalloc(q.data_ptr(), kv.data_ptr(), sink.data_ptr(), idx.data_ptr(), b, s, h, d,
+                                        kv.shape[1], idx.shape[2], float(scale), out.data_ptr(), _stream(stream),
+                                        k, sp))
     return out
 
 

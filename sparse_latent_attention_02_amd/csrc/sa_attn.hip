@@ -51,6 +51,7 @@
 #include "../../include/sparse_attn.h"
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 namespace {
@@ -1998,7 +1999,57 @@ KvRows kv8_rows(const uint8_t *kc, const uint8_t *ks) {
     return r;
 }
 
+// ---------------------------------------------------- allocation-free entry --
+//
+// Scratch of sa_sparse_attn_noalloc: the split variants' f32 partials, in a
+// device array of the library's own, so that the call allocates nothing.  Each
+// device the library runs on holds its own copy from the code object's load
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory: its device address (one per device) comes from
+// hipGetSymbolAddress, and only that address is ever handed to a kernel.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch's device address on the current device, looked up once per
+// device (with that device current); null if the lookup fails.
+void *scratch_address() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
+
+extern "C" size_t sa_sparse_attn_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+extern "C" sa_status sa_sparse_attn_noalloc(const uint16_t *q, const uint16_t *kv, const float *sink,
+                                            const int32_t *idx, int64_t b, int64_t s, int32_t h, int32_t d,
+                                            int64_t rows, int32_t topk, float scale, uint16_t *out, void *stream,
+                                            int32_t kernel, int32_t splits) {
+    // the variant and its partials' size exactly as sa_sparse_attn_ex takes them
+    size_t need = 0;
+    if (b >= 0 && s >= 0 && h > 0 && topk >= 0 && valid_d(d) && b * s > 0) {
+        Variant v;
+        sa_status st = resolve_variant(b * s, h, topk, kernel, splits, &v);
+        if (st != SA_OK) return st;
+        need = workspace_for(v, b * s, h, d);
+    }
+    if (need > kScratchBytes) return SA_ERR_SHAPE;
+    void *ws = nullptr;
+    if (need > 0 && !(ws = scratch_address())) return SA_ERR_HIP;
+    return run_sparse_attn(q, bf16_rows(kv), sink, idx, b, s, h, d, rows, topk, scale, out, ws,
+                           need > 0 ? kScratchBytes : 0, stream, kernel, splits);
+}
 
 extern "C" size_t sa_sparse_attn_workspace_bytes(int64_t b, int64_t s, int32_t h, int32_t d, int32_t topk) {
     if (b < 0 || s < 0 || h <= 0 || topk < 0 || !valid_d(d)) return 0;
