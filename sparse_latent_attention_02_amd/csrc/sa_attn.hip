@@ -650,7 +650,9 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
         for (int st = 0; st < nst; ++st) {
             asm volatile("s_waitcnt vmcnt(0)" : : : "memory");  // this wave's copies of stage st
             lds_barrier();  // everyone's copies in place; stage st-1 consumed, its buffer free
-            if (st > 0 && replay[(st - 1) & 1]) break;          // (no copy in flight here)
+            // the previous stage's replay flag, tested after the score product (see
+            // the pair kernel)
+            const int replay_prev = st > 0 ? replay[(st - 1) & 1] : 0;
             const SA_LDS char *buf = lds + ((st + 1) & 1) * C::STAGE_BYTES;
             const bool more = st + 1 < nst;
             const int rows_next = more ? stage_rows(st + 1) : 0;
@@ -680,6 +682,7 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
                 }
             }
 
+            if (replay_prev) break;
             // ---- weights and weighted sum of this wave's half of the stage ----
             slice_weights_pv<C>(sacc, st * C::ROWS + 32 * rh, nv, p.scale_log2, m_ref, m_seen, l_run, have_ref,
                                 replay[st & 1], buf, vlo, vhi, acc_o);
@@ -836,7 +839,7 @@ struct PairCfg {
     static constexpr int SMEM = std::max(NBUF * STAGE_BYTES, OUT_BYTES);
     static_assert(SMEM - OUT_BYTES >= 4 * D, "room for the rotation table row past the staged output");
     static constexpr float SLACK = 32.0f;
-    static constexpr int PFK = D > 256 ? 3 : 4;
+    static constexpr int PFK = 4;   // (the pair kernel's registers allow four at d = 512; the wide kernel's do not)
     static constexpr int PFV = D > 256 ? 2 : 3;
     static constexpr int PFV_EARLY = kPfvEarly;
     // the next stage's copies go out over the first quarter of the score product
@@ -1010,7 +1013,11 @@ __global__ void __launch_bounds__(128, 2) sa_attn_pair(const AttnParams p) {
         for (int st = 0; st < nst; ++st) {
             asm volatile("s_waitcnt vmcnt(0)" : : : "memory");  // this wave's copies of stage st
             lds_barrier();  // both waves' copies in place; stage st-1 consumed, its buffer free
-            if (st > 0 && replay[(st - 1) & 1]) break;          // (no copy in flight here)
+            // the previous stage's replay flag: read here, tested after the score
+            // product, so the LDS round trip overlaps it.  Copies of the next stage
+            // issued before a break land before any buffer is reused: the list
+            // chunk that restarts the pass waits for all of this wave's copies.
+            const int replay_prev = st > 0 ? replay[(st - 1) & 1] : 0;
             const SA_LDS char *buf = lds + (st & 1) * C::STAGE_BYTES;
             const bool more = st + 1 < nst;
             const int rows_next = more ? stage_rows(st + 1) : 0;
@@ -1037,6 +1044,7 @@ __global__ void __launch_bounds__(128, 2) sa_attn_pair(const AttnParams p) {
                 }
             }
 
+            if (replay_prev) break;
             // ---- weights and weighted sum of the stage ----
             slice_weights_pv<C>(sacc, st * C::ROWS, nv, p.scale_log2, m_ref, m_seen, l_run, have_ref, replay[st & 1],
                                 buf, vlo, vhi, acc_o);

@@ -7,45 +7,83 @@
 //    Attention.forward (window and compressed lists concatenated along topk) and
 //    the Indexer tail (reachable positions shifted by the window-row count,
 //    unreachable ones -1).
-// Integer fills, one thread per output entry; memory bound and negligible next to
-// the attention itself.
+// Integer fills: a grid of (column chunks) x (rows), four consecutive entries
+// per thread, written as one 16-byte store when the row layout allows it;
+// memory bound and small next to the attention itself.
 #include "sa_device.h"
 #include "../../include/sparse_attn.h"
 
+#include <algorithm>
+
 namespace {
 
-__global__ void window_idx_kernel(int32_t *__restrict__ out, int64_t n_out, int32_t nrows,
-                                  int32_t cols, int64_t row_stride, int32_t window,
-                                  int64_t start_pos) {
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= n_out) return;
-    const int32_t j = (int32_t)(t % cols);
-    const int64_t row = t / cols;                 // (batch, query row) flattened
-    const int32_t r = (int32_t)(row % nrows);     // query row within the chunk
-    int64_t slot, newest;
-    if (start_pos == 0) {
-        // causal window of the chunk ending at query r
-        const int64_t first = r - window + 1 > 0 ? (int64_t)r - window + 1 : 0;
-        slot = first + j;
-        newest = r;
+using namespace sa;
+
+// entries j0 .. j0 + 3 (those < cols) of row `row` at out_row, vectorised when `vec`
+__device__ __forceinline__ void store4(int32_t *out_row, int32_t j0, int32_t cols, bool vec, i32x4_t v) {
+    if (vec) {
+        *reinterpret_cast<i32x4_t *>(out_row + j0) = v;
     } else {
-        // ring listed oldest first: one past the newest slot, wrapping around
-        slot = (start_pos % window + 1 + j) % window;
-        newest = start_pos;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (j0 + i < cols) out_row[j0 + i] = v[i];
     }
-    out[row * row_stride + j] = slot > newest ? -1 : (int32_t)slot;
 }
 
-__global__ void append_idx_kernel(int32_t *__restrict__ out, int64_t row_stride, int32_t col0,
-                                  const int32_t *__restrict__ cidx, int64_t n_out, int32_t kc,
-                                  int32_t offset) {
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= n_out) return;
-    const int64_t r = t / kc;
-    const int32_t j = (int32_t)(t % kc);
-    const int32_t c = cidx[t];
-    out[r * row_stride + col0 + j] = c < 0 ? -1 : c + offset;
+// grid: x = chunks of 4 columns, y = query rows (strided), z = batch (strided)
+__global__ void window_idx_kernel(int32_t *__restrict__ out, int32_t bsz, int32_t nrows, int32_t cols,
+                                  int64_t row_stride, int32_t window, int64_t start_pos, bool vec) {
+    const int32_t j0 = (int32_t)(blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (j0 >= cols) return;
+    // decode: the ring listed oldest first, starting one past the newest slot
+    const int32_t oldest = start_pos > 0 ? (int32_t)(start_pos % window + 1) : 0;
+    for (int32_t b = blockIdx.z; b < bsz; b += gridDim.z) {
+        for (int32_t r = blockIdx.y; r < nrows; r += gridDim.y) {
+            i32x4_t v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int32_t j = j0 + i;
+                int64_t slot, newest;
+                if (start_pos == 0) {
+                    // causal window of the chunk ending at query r
+                    slot = (r - window + 1 > 0 ? r - window + 1 : 0) + j;
+                    newest = r;
+                } else {
+                    const int32_t s = oldest + j;   // < 2 window
+                    slot = s >= window ? s - window : s;
+                    newest = start_pos;
+                }
+                v[i] = slot > newest ? -1 : (int32_t)slot;
+            }
+            store4(out + ((int64_t)b * nrows + r) * row_stride, j0, cols, vec, v);
+        }
+    }
 }
+
+// grid: x = chunks of 4 compressed columns, y = rows (strided)
+__global__ void append_idx_kernel(int32_t *__restrict__ out, int64_t row_stride, int32_t col0,
+                                  const int32_t *__restrict__ cidx, int64_t n_rows, int32_t kc,
+                                  int32_t offset, bool vec) {
+    const int32_t j0 = (int32_t)(blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (j0 >= kc) return;
+    for (int64_t r = blockIdx.y; r < n_rows; r += gridDim.y) {
+        const int32_t *crow = cidx + r * kc;
+        i32x4_t c;
+        if (vec) {
+            c = *reinterpret_cast<const i32x4_t *>(crow + j0);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) c[i] = j0 + i < kc ? crow[j0 + i] : -1;
+        }
+        i32x4_t v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = c[i] < 0 ? -1 : c[i] + offset;
+        store4(out + r * row_stride + col0, j0, kc, vec, v);
+    }
+}
+
+constexpr int kIdxThreads = 256;
+constexpr int64_t kMaxGridYZ = 65535;
 
 }  // namespace
 
@@ -74,11 +112,11 @@ extern "C" sa_status sa_window_topk_idxs(int32_t window, int32_t bsz, int32_t se
     const int64_t n_out = (int64_t)bsz * nrows * cols;
     if (n_out == 0) return SA_OK;
     if (!idx) return SA_ERR_NULL;
-    const int threads = 256;
-    const int64_t blocks = (n_out + threads - 1) / threads;
-    if (blocks > 0x7fffffff) return SA_ERR_SHAPE;
-    hipLaunchKernelGGL(window_idx_kernel, dim3((unsigned)blocks), dim3(threads), 0,
-                       (hipStream_t)stream, idx, n_out, nrows, cols, row_stride, window, start_pos);
+    const bool vec = row_stride % 4 == 0 && cols % 4 == 0 && reinterpret_cast<uintptr_t>(idx) % 16 == 0;
+    const unsigned gx = (unsigned)((((int64_t)cols + 3) / 4 + kIdxThreads - 1) / kIdxThreads);
+    const dim3 grid(gx, (unsigned)std::min<int64_t>(nrows, kMaxGridYZ), (unsigned)std::min<int64_t>(bsz, kMaxGridYZ));
+    hipLaunchKernelGGL(window_idx_kernel, grid, dim3(kIdxThreads), 0, (hipStream_t)stream, idx, bsz, nrows, cols,
+                       row_stride, window, start_pos, vec);
     return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
@@ -90,11 +128,12 @@ extern "C" sa_status sa_append_compressed_idxs(int32_t *idx, int64_t row_stride,
     const int64_t n_out = n_rows * kc;
     if (n_out == 0) return SA_OK;
     if (!idx || !cidx) return SA_ERR_NULL;
-    const int threads = 256;
-    const int64_t blocks = (n_out + threads - 1) / threads;
-    if (blocks > 0x7fffffff) return SA_ERR_SHAPE;
-    hipLaunchKernelGGL(append_idx_kernel, dim3((unsigned)blocks), dim3(threads), 0,
-                       (hipStream_t)stream, idx, row_stride, col0, cidx, n_out, kc, offset);
+    const bool vec = row_stride % 4 == 0 && col0 % 4 == 0 && kc % 4 == 0 &&
+                     reinterpret_cast<uintptr_t>(idx) % 16 == 0 && reinterpret_cast<uintptr_t>(cidx) % 16 == 0;
+    const unsigned gx = (unsigned)((((int64_t)kc + 3) / 4 + kIdxThreads - 1) / kIdxThreads);
+    const dim3 grid(gx, (unsigned)std::min<int64_t>(n_rows, kMaxGridYZ));
+    hipLaunchKernelGGL(append_idx_kernel, grid, dim3(kIdxThreads), 0, (hipStream_t)stream, idx, row_stride, col0,
+                       cidx, n_rows, kc, offset, vec);
     return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
