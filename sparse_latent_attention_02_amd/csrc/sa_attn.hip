@@ -83,6 +83,7 @@ struct AttnParams {
     int32_t split_len;  // index entries per split
     float scale_log2;   // softmax scale * log2(e)
     int32_t stagger_cu; // pair kernel: workgroups [stagger_cu, 2 stagger_cu) start late (0: none)
+    int32_t qchunk;     // wide and pair kernels: consecutive queries per XCD run (see wide_unit)
     // fused decode step only: the list is built in the kernel and the step's
     // new latent row is rounded through fp8 and written into its ring slot
     const uint16_t *kv_new;  // [nq][d] this step's raw latent rows
@@ -217,21 +218,31 @@ __device__ __forceinline__ uint32_t logical_wg(uint32_t T) {
     return x < rem ? x * (per + 1) + k : rem * (per + 1) + (x - rem) * per + k;
 }
 
-// Wide-kernel workgroup -> (query, j = head group * n_sp + split); false for a
-// padding workgroup.  The dispatcher hands block b to XCD b % 8, each XCD taking
-// its blocks in order.  A query's n_hg * n_sp workgroups are consecutive blocks
-// of one XCD (they gather the same rows: the later ones hit that XCD's L2);
-// queries are dealt to the XCDs in turn, so lists whose length grows with the
-// query position (a causal prefill) load every XCD alike; and the highest query
-// index goes first (the longest list of a causal prefill: long work first leaves
-// short work for the tail).  The grid holds 8 * ceil(nq / 8) queries' worth of
-// workgroups.
+// Wide/pair-kernel workgroup -> (query, j = head group * n_sp + split); false
+// for a padding workgroup.  The dispatcher hands block b to XCD b % 8, each XCD
+// taking its blocks in order.  A query's n_hg * n_sp workgroups are consecutive
+// blocks of one XCD (they gather the same rows: the later ones hit that XCD's
+// L2).  Queries go to the XCDs in runs of qchunk consecutive queries, eight runs
+// a round in serpentine order (XCD 0..7, then 7..0), so lists whose length grows
+// with the query position (a causal prefill) load every XCD alike; within an
+// XCD the highest query index goes
+// first (long work first leaves short work for the tail).  Runs of more than one
+// query serve long prefills: neighbouring queries' windows share most of their
+// rows, so an XCD's run fetches them into its L2 once instead of every XCD
+// fetching every row.  The grid holds 8 * qchunk * ceil(nq / (8 * qchunk))
+// queries' worth of workgroups.
 __device__ __forceinline__ bool wide_unit(const AttnParams &p, uint32_t &qi, uint32_t &j) {
     const uint32_t g = (uint32_t)(p.n_hg * p.n_sp);
     const uint32_t k = blockIdx.x >> 3, m = k / g;
     j = k - m * g;
-    const uint32_t rounds = ((uint32_t)p.nq + 7u) >> 3;
-    qi = 8u * (rounds - 1u - m) + (blockIdx.x & 7u);
+    const uint32_t C = (uint32_t)p.qchunk;
+    const uint32_t runs = ((uint32_t)p.nq + 8u * C - 1u) / (8u * C);   // runs per XCD
+    const uint32_t r = m / C, w = m - r * C;
+    // round R of eight runs (highest first) goes to the XCDs in serpentine order,
+    // so the XCDs' shares of a causal prefill's growing lists stay even
+    const uint32_t R = runs - 1u - r, x = blockIdx.x & 7u;
+    const uint32_t run = 8u * R + ((R & 1u) ? 7u - x : x);
+    qi = run * C + (C - 1u - w);
     return qi < (uint32_t)p.nq;
 }
 
@@ -570,7 +581,7 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
         const int hd = (int)hg * C::HEADS + hl;
         if (hd < p.h) {
             if (chunk_lane)
-                dma_16B(p.q + ((int64_t)qi * p.h + hd) * D + (lane ^ C::L::swz(hl)) * 8, smem_base + hl * C::RS);
+                dma_16B_nt(p.q + ((int64_t)qi * p.h + hd) * D + (lane ^ C::L::swz(hl)) * 8, smem_base + hl * C::RS);
         } else if (chunk_lane) {
             *reinterpret_cast<SA_LDS u32x4_t *>((SA_LDS char *)smem + hl * C::RS + 16 * lane) =
                 u32x4_t{0u, 0u, 0u, 0u};
@@ -799,7 +810,7 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
         if (hglob < p.h && chunk_lane) {
             u32x4_t v = *reinterpret_cast<const SA_LDS u32x4_t *>(stg + hr * C::L::OUT_RS + 16 * lane);
             if (rot) v = unrotate_chunk(v, 8 * lane, D, p.rope_dim, (const SA_LDS float *)rtab);
-            *reinterpret_cast<u32x4_t *>(p.out + ((int64_t)qi * p.h + hglob) * D + lane * 8) = v;
+            store_16B_nt(p.out + ((int64_t)qi * p.h + hglob) * D + lane * 8, v);
         }
     }
 }
@@ -926,7 +937,7 @@ __global__ void __launch_bounds__(128, 2) sa_attn_pair(const AttnParams p) {
     for (int u = 0; u < 32; ++u) {
         const int hd = ((int)hg * 2 + wave) * 32 + u;
         if (chunk_lane)
-            dma_16B(p.q + ((int64_t)qi * p.h + (hd < p.h ? hd : 0)) * D + (lane ^ C::L::swz(u)) * 8,
+            dma_16B_nt(p.q + ((int64_t)qi * p.h + (hd < p.h ? hd : 0)) * D + (lane ^ C::L::swz(u)) * 8,
                     smem_base + (uint32_t)((wave * 32 + u) * C::RS));
     }
     if (has_new && wave == 0) {
@@ -1124,7 +1135,7 @@ __global__ void __launch_bounds__(128, 2) sa_attn_pair(const AttnParams p) {
             if (hglob < p.h && chunk_lane) {
                 u32x4_t w = v[i];
                 if (rot) w = unrotate_chunk(w, 8 * lane, D, p.rope_dim, rtab);
-                *reinterpret_cast<u32x4_t *>(p.out + ((int64_t)qi * p.h + hglob) * D + lane * 8) = w;
+                store_16B_nt(p.out + ((int64_t)qi * p.h + hglob) * D + lane * 8, w);
             }
         }
     }
@@ -1366,7 +1377,7 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
             const int head = (int)hg * C::HEADS + hl;
             if (head < p.h) {
                 if (chunk_lane)
-                    dma_16B(p.q + ((int64_t)qi * p.h + head) * D + lane * 8,
+                    dma_16B_nt(p.q + ((int64_t)qi * p.h + head) * D + lane * 8,
                             __builtin_amdgcn_readfirstlane(q_base + hl * C::RS));
             } else if (chunk_lane) {
                 *reinterpret_cast<SA_LDS u32x4_t *>((SA_LDS char *)qbuf + hl * C::RS + 16 * lane) =
@@ -1617,7 +1628,7 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
         if (hglob < p.h && chunk_lane) {
             u32x4_t v = *reinterpret_cast<const SA_LDS u32x4_t *>((const SA_LDS char *)qbuf + hr * C::RS + 16 * lane);
             if (rot) v = unrotate_chunk(v, 8 * lane, D, p.rope_dim, (const SA_LDS float *)rtab);
-            *reinterpret_cast<u32x4_t *>(p.out + ((int64_t)qi * p.h + hglob) * D + lane * 8) = v;
+            store_16B_nt(p.out + ((int64_t)qi * p.h + hglob) * D + lane * 8, v);
         }
     }
 }
@@ -1704,6 +1715,8 @@ void set_splits(Variant &v, int32_t topk, int n_sp) {
 // pass) only when the chosen kernel would leave CUs idle and the list is long
 // enough to share.
 constexpr int kDecodeMaxTopk = 512;
+constexpr int kQueryRun = 128;            // consecutive queries per XCD run (prefill chunks)
+constexpr int kQueryRunMinQueries = 4096; // chunk length from which queries go in runs (>= 4 runs per XCD)
 constexpr int kPairMinPerCu = 4;
 constexpr int kPairShortList = 512;   // pair kernel list chunk for lists up to this many entries
 constexpr int kPairLongList = 2176;   // and for longer ones (a 128 + 2048-entry list in one pass)
@@ -1864,7 +1877,12 @@ AttnParams base_params(const uint16_t *q, const uint16_t *kv, const float *sink,
 template <bool FUSED, bool KV8>
 sa_status enqueue(AttnParams &p, const Variant &v, int32_t d, hipStream_t hs) {
     // decode kernel: one block per workgroup; wide and pair kernels: 8 * ceil(nq / 8) queries' worth
-    const int64_t units = v.kernel == SA_KERNEL_DECODE ? (int64_t)p.nq : 8 * (((int64_t)p.nq + 7) / 8);
+    // wide and pair kernels: queries dealt to the XCDs in runs (see wide_unit) --
+    // runs of kQueryRun for a chunk of at least kQueryRunMinQueries queries of one
+    // sequence (windows of neighbouring queries overlap), single queries otherwise
+    p.qchunk = (v.kernel != SA_KERNEL_DECODE && p.s >= kQueryRunMinQueries) ? kQueryRun : 1;
+    const int64_t run8 = 8 * (int64_t)p.qchunk;
+    const int64_t units = v.kernel == SA_KERNEL_DECODE ? (int64_t)p.nq : run8 * (((int64_t)p.nq + run8 - 1) / run8);
     const int64_t total = units * p.n_hg * v.n_sp;
     if (total > 0x7fffffffLL) return SA_ERR_SHAPE;
     p.total_wg = (int32_t)total;

@@ -69,12 +69,23 @@ __device__ __forceinline__ void dma_16B(const void *src, uint32_t lds_base) {
                  : "memory", "m0");
 }
 
+// The same copy with the non-temporal hint, for data read once (a query's head
+// rows, its index list): it is kept from displacing the latent rows that many
+// workgroups of an XCD share in its L2.
+__device__ __forceinline__ void dma_16B_nt(const void *src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+                 :
+                 : "v"(src), "s"(lds_base)
+                 : "memory", "m0");
+}
+
 // Direct global -> LDS copy of one 4-byte value per lane (gfx950
 // global_load_lds_dword): lane i's value lands at lds_base + 4 i (inactive lanes
-// write nothing).  Completion is tracked by the caller's vmcnt waits; the
-// M0 wait state as in dma_16B.
+// write nothing), with the non-temporal hint (index lists are read once).
+// Completion is tracked by the caller's vmcnt waits; the M0 wait state as in
+// dma_16B.
 __device__ __forceinline__ void dma_4B(const void *src, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off nt"
                  :
                  : "v"(src), "s"(lds_base)
                  : "memory", "m0");
@@ -97,6 +108,12 @@ __device__ __forceinline__ void wait_all_barrier() {
 // Wait for this wave's LDS operations, then barrier the workgroup.
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+}
+
+// 16-byte store of a result read by no later workgroup, with the
+// non-temporal hint (streamed out without displacing shared rows in L2)
+__device__ __forceinline__ void store_16B_nt(void *dst, u32x4_t v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(dst));
 }
 
 __device__ __forceinline__ float shfl_xor_f32(float v, int mask) {

@@ -1,7 +1,7 @@
 """Host-side check of the built library's gfx950 code (no GPU needed).
 
-Every direct global->LDS copy (global_load_lds_*) takes its LDS address from
-M0.  On gfx950 such a copy needs one wait state after an SALU write of M0;
+Every direct global->LDS copy (global_load_lds_*, or buffer_load_* ... lds)
+takes its LDS address from M0.  On gfx950 such a copy needs one wait state after an SALU write of M0;
 without it the copy can take the previous M0 and land its row in the previous
 copy's slot.  The copies are issued from inline asm, which the compiler does not
 look into, so the asm carries the wait state itself.  This test disassembles
@@ -58,7 +58,8 @@ def gfx950_instructions(tmp_path):
 
 def test_every_lds_copy_waits_after_setting_m0(tmp_path):
     ins = gfx950_instructions(tmp_path)
-    copies = [i for i, x in enumerate(ins) if x.startswith("global_load_lds")]
+    copies = [i for i, x in enumerate(ins)
+              if x.startswith("global_load_lds") or (x.startswith("buffer_load") and x.split()[-1] == "lds")]
     assert len(copies) > 100, "the attention kernels' copies are missing from the disassembly"
     bad = []
     for i in copies:

@@ -126,6 +126,23 @@ def test_sparse_attn_small(case, variant):
     assert_parity(got, ref, f"case {case} variant {variant}")
 
 
+@pytest.mark.parametrize("b,s", [(1, 4100), (2, 4099)], ids=["one_sequence", "two_sequences"])
+@pytest.mark.parametrize("variant", [None, (1, 1), (3, 2)], ids=lambda v: "auto" if v is None else "k%d_sp%d" % v)
+def test_sparse_attn_long_chunks_in_xcd_runs(b, s, variant):
+    """Chunks of 4096 or more queries go to the XCDs in runs of consecutive queries
+    (the grid padded to whole runs): a ragged query count, and runs that straddle
+    two sequences, every query compared with the oracle, output pre-filled with NaN."""
+    print(f"xcd runs b={b} s={s} variant {variant}", flush=True)
+    c = wl.small_case(40 + b, b, s, 16, 64, 300, 48, p_invalid=0.1)
+    q, kv, sink, idx = to_dev(c["q"]), to_dev(c["kv"]), to_dev(c["sink"]), to_dev(c["idx"])
+    out = torch.full_like(q, float("nan"))
+    sa.sparse_attn(q, kv, sink, idx, 0.125, out=out, variant=variant)
+    torch.cuda.synchronize()
+    _, ref32 = oracle.sparse_attn(bits(c["q"]), bits(c["kv"]), c["sink"].numpy(), c["idx"].numpy(), 0.125,
+                                  want_f32=True)
+    assert_parity(bits(out), ref32, f"xcd runs b={b} s={s} {variant}")
+
+
 @pytest.mark.parametrize("d", [64, 512])
 @pytest.mark.parametrize("variant", [None, (1, 1), (1, 2), (2, 1), (3, 1), (3, 2)], ids=lambda v: "auto" if v is None else "k%d_sp%d" % v)
 def test_sparse_attn_scores_outrunning_the_first_stage(d, variant):
