@@ -26,11 +26,13 @@ Inputs are resident in HBM before the timed region.  Small workloads rotate
 through enough independently generated input sets (more than twice the 256 MiB
 MALL) that every step reads its inputs from HBM, not from cache.
 
-The steps over the rotating input sets are captured as one chain in a HIP graph
-and replayed, so the host's launch cost stays out of the measurement
-(``--no-graphs`` launches eagerly).  The attention kernel's duration is taken
-with HIP events on the launch stream around a graph of back-to-back attention
-launches alone (one per input set).
+The steps are captured as a chain in a HIP graph -- at least 32 steps, cycling
+through the input sets -- and replayed, so the host's launch cost stays out of
+the measurement (``--no-graphs`` launches eagerly).  The attention kernel's
+duration is taken with HIP events on the launch stream around a graph of the
+same number of back-to-back attention launches alone.  ``--sets 1`` keeps one
+input set resident instead, to measure the same step with its inputs warm in
+the caches.
 
 Prints one JSON line: throughput (query-heads/s), the roofline position of the
 attention kernel, and the CPU oracle timed on a bounded sample of the same
@@ -50,6 +52,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 MALL_BYTES = 256 << 20
+CHAIN_MIN = 32                 # steps per captured graph, at least
 
 
 def parse():
@@ -57,10 +60,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=5, choices=[2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5],
+                    help="1 (the tiny ring run) only with --cpu-only")
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-only", action="store_true",
+                    help="time only the CPU oracle on the workload (threads from OMP_NUM_THREADS, else all "
+                         "cores) and print its JSON object; no GPU is used")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration under rocprofv3)")
     ap.add_argument("--unfused", action="store_true",
@@ -154,7 +161,11 @@ def cpu_baseline(wid, target_s):
     w = wl.WORKLOADS[wid]
     raw = wl.generate(wid)
     bits = wl.bf16_bits
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    # the oracle's OpenMP loops get this many threads, set explicitly (another
+    # OpenMP runtime in the process, torch's, may have fixed its own count)
+    threads = oracle.set_threads(int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0)))
+    if wid == 1:
+        return ring_run_baseline(w, raw, threads, target_s)
     sink = raw["sink"].numpy()
     comp = np.ascontiguousarray(raw["comp"].numpy()) if raw["comp"] is not None else None
 
@@ -229,6 +240,45 @@ def cpu_baseline(wid, target_s):
                       f"attention); {t:.2f} s"}
 
 
+def ring_run_baseline(w, raw, threads, target_s):
+    """The oracle over the tiny ring run: a 12-token prefill written into an
+    8-slot ring, then decode steps at positions 12 and 13 (fp8 round trip of the
+    new rows, ring write, window lists, attention), repeated to the target time."""
+    import numpy as np
+    import oracle
+    from sparse_latent_attention_02_amd import workloads as wl
+    bits = wl.bf16_bits
+    sink = raw["sink"].numpy()
+    q_pre, kv_pre = bits(raw["q_prefill"]), bits(raw["kv_prefill"])
+    q_dec = [bits(raw["q_dec"][i]) for i in range(2)]
+    kv_dec = [bits(raw["kv_dec"][i]) for i in range(2)]
+
+    def run():
+        chunk = kv_pre.copy()
+        oracle.act_quant_fp8_inplace(chunk)
+        ring = np.zeros((1, w.window, w.d), dtype=np.uint16)
+        oracle.ring_write(ring, chunk, 0)
+        oracle.sparse_attn(q_pre, chunk, sink, oracle.window_topk_idxs(w.window, 1, 12, 0), w.scale)
+        for i, pos in enumerate((12, 13)):
+            row = kv_dec[i].copy()
+            oracle.act_quant_fp8_inplace(row)
+            oracle.ring_write(ring, row, pos)
+            oracle.sparse_attn(q_dec[i], ring, sink, oracle.window_topk_idxs(w.window, 1, 1, pos), w.scale)
+
+    run()
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        run()
+        passes += 1
+        el = time.perf_counter() - t0
+        if el > target_s or passes >= 100000:
+            break
+    qh = (12 + 2) * w.h
+    return {"value": passes * qh / el, "unit": "query-heads/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole ring run (prefill 12, decode 12 and 13; {qh} query-heads), {passes} passes; "
+                      f"{el:.2f} s"}
+
+
 def copy_calibration():
     """A plain streaming copy of known size (1 GiB read, 1 GiB written) with the
     same 16-byte-per-lane access width as the kernels, for scaling the HBM byte
@@ -299,7 +349,7 @@ def bench_select(args):
     }
     if not args.no_cpu_baseline:
         import oracle
-        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+        threads = oracle.set_threads(int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0)))
         sc = wl.indexer_scores(3000, b, s, T).numpy()
         t0 = time.perf_counter()
         passes = 0
@@ -320,6 +370,14 @@ def main():
     if args.gpus != 1 or world != 1:
         print("bench.py: this build measures one GPU; runs over several GPUs are not part of it "
               "(sparse_attn shards over batch/queries or heads with no exchange step).", file=sys.stderr)
+        sys.exit(2)
+
+    if args.cpu_only:
+        line = {"workload": args.workload, "cpu_baseline": cpu_baseline(args.workload, args.cpu_seconds)}
+        print(json.dumps(line), flush=True)
+        return
+    if args.workload == 1:
+        print("bench.py: workload 1 is timed with --cpu-only only (it is a correctness case)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -383,21 +441,25 @@ def main():
                 for i in ids:
                     fn(sets[i])
             return g
-        full = capture(step_fn, range(n_sets))
-        rem = args.steps % n_sets
-        tail = capture(step_fn, range(rem)) if rem else None
+        # (a chain of at least CHAIN_MIN steps, cycling through the sets, so that
+        # a single resident set is not timed one graph launch per step)
+        chain = n_sets * max(1, math.ceil(CHAIN_MIN / n_sets))
+        ids = [i % n_sets for i in range(chain)]
+        full = capture(step_fn, ids)
+        rem = args.steps % chain
+        tail = capture(step_fn, ids[:rem]) if rem else None
 
         def run_steps(k):
-            for _ in range(k // n_sets):
+            for _ in range(k // chain):
                 full.replay()
-            if k % n_sets:
-                assert k % n_sets == rem
+            if k % chain:
+                assert k % chain == rem
                 tail.replay()
-        attn_graph = capture(kern_fn, range(n_sets))
-        n_attn_reps = max(1, math.ceil(args.steps / n_sets))
+        attn_graph = capture(kern_fn, ids)
+        n_attn_reps = max(1, math.ceil(args.steps / chain))
         run_attn = lambda: [attn_graph.replay() for _ in range(n_attn_reps)]
-        n_attn = n_attn_reps * n_sets
-        launch_desc = f"hip graph of {n_sets} steps"
+        n_attn = n_attn_reps * chain
+        launch_desc = f"hip graph of {chain} steps over the {n_sets} input set{'s' if n_sets > 1 else ''}"
     else:
         def run_steps(k):
             for i in range(k):

@@ -65,12 +65,19 @@ def lib() -> ctypes.CDLL:
         L.sao_sparse_attn.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i64, i32, f32, vp, vp]
         L.sao_apply_rotary.argtypes = [vp, i64, i64, i32, i32, i32, vp, i64, i64, ctypes.c_int]
         L.sao_indexer_topk.argtypes = [vp, i64, i64, i32, i64, i32, i32, i32, vp, i64, i32]
+        L.sao_set_threads.argtypes = [ctypes.c_int]
         for name in ("sao_window_topk_idxs_shape", "sao_window_topk_idxs", "sao_ring_write",
                      "sao_act_quant_fp8_inplace", "sao_append_compressed_idxs", "sao_sparse_attn",
-                     "sao_kv8_pack", "sao_kv8_unpack", "sao_apply_rotary", "sao_indexer_topk"):
+                     "sao_kv8_pack", "sao_kv8_unpack", "sao_apply_rotary", "sao_indexer_topk", "sao_set_threads"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
+
+
+def set_threads(n: int = 0) -> int:
+    """Thread count of the oracle's parallel loops (n > 0 sets it); returns the
+    count they use from now on."""
+    return int(lib().sao_set_threads(int(n)))
 
 
 def _ptr(a):

@@ -28,6 +28,7 @@
  * Build: gcc -O2 -std=c11 -fopenmp -ffp-contract=off -fPIC -shared
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stddef.h>
 #include <stdlib.h>
@@ -505,4 +506,11 @@ int sao_indexer_topk(const float *scores, int64_t b, int64_t s, int32_t T, int64
         free(sel);
     }
     return bad ? SAO_ERR_UNSUPPORTED : SAO_OK;
+}
+
+/* Thread count of the OpenMP loops above: n > 0 sets it; returns the count a
+ * parallel loop will use from now on (timing support, no arithmetic). */
+int sao_set_threads(int n) {
+    if (n > 0) omp_set_num_threads(n);
+    return omp_get_max_threads();
 }
