@@ -819,8 +819,9 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
 //
 // Pair kernel: one workgroup of two wavefronts per (query, 64 heads[, index
 // split]), for grids of many workgroups (prefill).  Each wavefront owns a
-// 32-head tile over the whole head dim (Q in registers, loaded straight from
-// memory: no other wavefront needs it; O in accumulator registers) and walks
+// 32-head tile over the whole head dim (Q in registers, its 32 head rows copied
+// by the wavefront itself through the stage buffers; O in accumulator
+// registers) and walks
 // every row of the list in 32-row stages: S^T[32 rows][32 heads] = K Q^T, the
 // softmax against the fixed reference of the wide kernel, O^T[d][32 heads] +=
 // V^T P^T, all on MFMA 32x32x16 with the operand layouts of the wide kernel.
@@ -854,8 +855,8 @@ struct PairCfg {
     static constexpr int PFV = D > 256 ? 2 : 3;
     static constexpr int PFV_EARLY = kPfvEarly;
     // the next stage's copies go out over the first quarter of the score product
-    // (measured a little faster here than an even spread: two workgroups share
-    // the CU's memory pipeline, and the copies start their flight sooner)
+    // (so they start their flight early; spreading them over half or all of it
+    // measured the same once the rows come from L2)
     static constexpr int copy_at(int i) { return std::min(RPW, (4 * i * RPW + KS - 1) / KS); }
     static_assert(KS >= 4 && DT >= 2 && RPW == 16, "tiling");
 };

@@ -39,17 +39,28 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 }
 constexpr uint32_t kKeyNegInf = 0x007fffffu;  // order_key(-inf)
 
+// Inclusive prefix sum over a wavefront, in lane order: within each row of 16
+// lanes, four steps over DPP row shifts by 1, 2, 4 and 8 (a lane shifted in from
+// outside the row reads 0), then each row adds the totals of the rows before it
+// (lanes 15, 31, 47).  VALU only: no LDS round trip.
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
+    const int row = (threadIdx.x & 63) >> 4;
+    return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+
 // Inclusive prefix sum over the workgroup of v (each thread's value, in thread
 // order); the total goes to *total.  Uses sums[kSelThreads / 64] in LDS; all
 // threads call it.
 __device__ __forceinline__ uint32_t wg_inclusive_sum(uint32_t v, uint32_t *sums, uint32_t *total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
+    const uint32_t x = wave_inclusive_sum(v);
     if (lane == 63) sums[wave] = x;
     __syncthreads();
     uint32_t before = 0, all = 0;
