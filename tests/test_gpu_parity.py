@@ -143,7 +143,7 @@ def test_sparse_attn_long_chunks_in_xcd_runs(b, s, variant):
     assert_parity(bits(out), ref32, f"xcd runs b={b} s={s} {variant}")
 
 
-@pytest.mark.parametrize("d", [64, 512])
+@pytest.mark.parametrize("d", [64, 256, 512])
 @pytest.mark.parametrize("variant", [None, (1, 1), (1, 2), (2, 1), (3, 1), (3, 2)], ids=lambda v: "auto" if v is None else "k%d_sp%d" % v)
 def test_sparse_attn_scores_outrunning_the_first_stage(d, variant):
     """The wide kernel takes the weights against the first max it sees and replays the
@@ -168,7 +168,7 @@ def test_sparse_attn_scores_outrunning_the_first_stage(d, variant):
     assert np.allclose(r, kv[:, 250].float().numpy(), rtol=2e-2, atol=2e-2)
 
 
-@pytest.mark.parametrize("d", [64, 128, 512])
+@pytest.mark.parametrize("d", [64, 128, 256, 512])
 @pytest.mark.parametrize("topk", [64, 130])
 @pytest.mark.parametrize("variant", [None, (1, 1), (1, 2), (2, 1), (2, 2), (3, 1), (3, 2)],
                          ids=lambda v: "auto" if v is None else "k%d_sp%d" % v)
