@@ -370,11 +370,12 @@ struct Compactor {
 //    head n; rows at or past the list end (entry ebase + row >= nv) weigh 0.
 //  * Weights are 2^(scale log2(e) s - m_ref) against a fixed reference: the
 //    first slice holding a valid row sets m_ref to its own max.  Later slices
-//    take their weights at once and compare their max with the reference only
-//    behind the first MFMA of the weighted sum: a max past it by more than
-//    SLACK (weights up to 2^SLACK stay far inside bf16 and f32 range) raises
-//    the replay flag, and the workgroup replays the list against the larger
-//    max, so O is never rescaled inside the loop.
+//    take their weights at once and compare their exponents with SLACK only
+//    behind the first MFMA of the weighted sum (one ballot; the cross-half max
+//    is taken only when it fires): an exponent past SLACK (weights up to
+//    2^SLACK stay far inside bf16 and f32 range) raises the replay flag, and
+//    the workgroup replays the list against the larger max, so O is never
+//    rescaled inside the loop.
 //  * The running sum adds the weights as rounded to bf16, as the MFMA takes them.
 //  * The first operand reads of the weighted sum go out before the weights:
 //    they do not depend on them.  MFMA j = kk DT + dt reads, in 16-lane group
@@ -446,14 +447,16 @@ __device__ __forceinline__ void slice_weights_pv(const f32x16_t &sacc, int ebase
         if (j + PF < NJ) vq[j % PF] = vread(j + PF);
         acc_o[j % C::DT] =
             __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, j >= C::DT ? pb1 : pb0, acc_o[j % C::DT], 0, 0, 0);
-        if (j == 0 && check) {
-            // a slice max past the reference by more than SLACK: replay against the larger max
+        if (j == 0 && check && __ballot(mt > C::SLACK)) {
+            // a slice exponent past SLACK in some lane: replay against the larger
+            // max.  The head's max over both row halves and the new reference are
+            // taken only here: a head's earlier slices that did not trigger stayed
+            // within SLACK of its reference, and the new one is never lower, so the
+            // replayed pass keeps every weight within 2^SLACK as well.
             mt = max_xor32(mt);
             m_seen = fmaxf(m_seen, m_ref + mt);
-            if (__ballot(mt > C::SLACK)) {
-                if (lane == 0) replay_flag = 1;
-                m_ref = m_seen;
-            }
+            if (lane == 0) replay_flag = 1;
+            m_ref = m_seen;
         }
         // the running sum over the weights behind MFMAs 1 .. NJ-1, in order
         if (j >= 1) {
