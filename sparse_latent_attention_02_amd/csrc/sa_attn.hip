@@ -1952,6 +1952,7 @@ sa_status run_sparse_attn(const uint16_t *q, const KvRows &kv, const float *sink
                           void *stream, int32_t kernel, int32_t splits, const Rope &rope = Rope()) {
     if (b < 0 || s < 0 || h < 0 || d < 0 || rows < 0 || topk < 0) return SA_ERR_SHAPE;
     if (!valid_d(d)) return SA_ERR_UNSUPPORTED;
+    if (!mul_le(b, s, 0x7fffffffLL)) return SA_ERR_SHAPE;
     const int64_t nq = b * s;
     if (check_rope(rope, d, s) != SA_OK) return SA_ERR_SHAPE;
     if (nq == 0 || h == 0) return SA_OK;
@@ -2068,7 +2069,7 @@ extern "C" sa_status sa_sparse_attn_noalloc(const uint16_t *q, const uint16_t *k
                                             int32_t kernel, int32_t splits) {
     // the variant and its partials' size exactly as sa_sparse_attn_ex takes them
     size_t need = 0;
-    if (b >= 0 && s >= 0 && h > 0 && topk >= 0 && valid_d(d) && b * s > 0) {
+    if (b >= 0 && s >= 0 && h > 0 && topk >= 0 && valid_d(d) && mul_le(b, s, 0x7fffffffLL) && b * s > 0) {
         Variant v;
         sa_status st = resolve_variant(b * s, h, topk, kernel, splits, &v);
         if (st != SA_OK) return st;
@@ -2082,7 +2083,7 @@ extern "C" sa_status sa_sparse_attn_noalloc(const uint16_t *q, const uint16_t *k
 }
 
 extern "C" size_t sa_sparse_attn_workspace_bytes(int64_t b, int64_t s, int32_t h, int32_t d, int32_t topk) {
-    if (b < 0 || s < 0 || h <= 0 || topk < 0 || !valid_d(d)) return 0;
+    if (b < 0 || s < 0 || h <= 0 || topk < 0 || !valid_d(d) || !mul_le(b, s, 0x7fffffffLL)) return 0;
     Variant v;
     if (resolve_variant(b * s, h, topk, 0, 0, &v) != SA_OK) return 0;
     return workspace_for(v, b * s, h, d);
@@ -2090,7 +2091,7 @@ extern "C" size_t sa_sparse_attn_workspace_bytes(int64_t b, int64_t s, int32_t h
 
 extern "C" size_t sa_sparse_attn_workspace_bytes_ex(int64_t b, int64_t s, int32_t h, int32_t d, int32_t topk,
                                                     int32_t kernel, int32_t splits) {
-    if (b < 0 || s < 0 || h <= 0 || topk < 0 || !valid_d(d)) return 0;
+    if (b < 0 || s < 0 || h <= 0 || topk < 0 || !valid_d(d) || !mul_le(b, s, 0x7fffffffLL)) return 0;
     Variant v;
     if (resolve_variant(b * s, h, topk, kernel, splits, &v) != SA_OK) return 0;
     return workspace_for(v, b * s, h, d);
@@ -2132,7 +2133,7 @@ extern "C" sa_status sa_sparse_attn_decode_step(const uint16_t *q, uint16_t *kv,
 
 extern "C" size_t sa_sparse_attn_kv8_workspace_bytes(int64_t b, int64_t s, int32_t h, int32_t d, int32_t topk,
                                                      int32_t splits) {
-    if (b < 0 || s < 0 || h <= 0 || topk < 0 || !valid_d(d)) return 0;
+    if (b < 0 || s < 0 || h <= 0 || topk < 0 || !valid_d(d) || !mul_le(b, s, 0x7fffffffLL)) return 0;
     Variant v;
     if (resolve_variant_kv(b * s, h, topk, 0, splits, true, &v) != SA_OK) return 0;
     return workspace_for(v, b * s, h, d);

@@ -2,7 +2,7 @@
 //
 // Vector types for MFMA operands, bf16 bit conversions, the direct global->LDS
 // copy (one 16-byte chunk per lane) and the explicit wait/barrier primitives the
-// gather pipeline relies on.
+// gather pipeline relies on; one host-side size check.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -119,5 +119,9 @@ __device__ __forceinline__ void store_16B_nt(void *dst, u32x4_t v) {
 __device__ __forceinline__ float shfl_xor_f32(float v, int mask) {
     return __shfl_xor(v, mask, 64);
 }
+
+// Host-side size check: a * b <= limit for non-negative a, b, without forming a
+// product that could overflow (entry points reject sizes past it before any launch).
+inline bool mul_le(int64_t a, int64_t b, int64_t limit) { return a == 0 || b <= limit / a; }
 
 }  // namespace sa

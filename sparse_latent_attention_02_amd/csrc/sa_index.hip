@@ -108,7 +108,7 @@ extern "C" sa_status sa_window_topk_idxs(int32_t window, int32_t bsz, int32_t se
     int32_t nrows = 0, cols = 0;
     sa_status st = sa_window_topk_idxs_shape(window, seqlen, start_pos, &nrows, &cols);
     if (st != SA_OK) return st;
-    if (bsz < 0 || row_stride < cols) return SA_ERR_SHAPE;
+    if (bsz < 0 || row_stride < cols || !mul_le((int64_t)bsz * nrows, cols, 0x7fffffffLL * 256)) return SA_ERR_SHAPE;
     const int64_t n_out = (int64_t)bsz * nrows * cols;
     if (n_out == 0) return SA_OK;
     if (!idx) return SA_ERR_NULL;
@@ -123,7 +123,8 @@ extern "C" sa_status sa_window_topk_idxs(int32_t window, int32_t bsz, int32_t se
 extern "C" sa_status sa_append_compressed_idxs(int32_t *idx, int64_t row_stride, int32_t col0,
                                                const int32_t *cidx, int64_t n_rows, int32_t kc,
                                                int32_t offset, void *stream) {
-    if (n_rows < 0 || kc < 0 || col0 < 0 || offset < 0 || row_stride < (int64_t)col0 + kc)
+    if (n_rows < 0 || kc < 0 || col0 < 0 || offset < 0 || row_stride < (int64_t)col0 + kc ||
+        !mul_le(n_rows, kc, 0x7fffffffLL * 256))
         return SA_ERR_SHAPE;
     const int64_t n_out = n_rows * kc;
     if (n_out == 0) return SA_OK;

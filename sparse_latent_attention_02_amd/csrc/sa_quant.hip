@@ -90,7 +90,8 @@ __global__ void __launch_bounds__(256) kv8_unpack_kernel(const uint8_t *__restri
 
 extern "C" sa_status sa_act_quant_fp8_inplace(uint16_t *x, int64_t n_rows, int32_t row_len,
                                               void *stream) {
-    if (n_rows < 0 || row_len <= 0 || row_len % 32 != 0) return SA_ERR_SHAPE;
+    if (n_rows < 0 || row_len <= 0 || row_len % 32 != 0 || !mul_le(n_rows, row_len / 8, 0x7fffffffLL * 256))
+        return SA_ERR_SHAPE;
     if (n_rows == 0) return SA_OK;
     if (!x) return SA_ERR_NULL;
     if (reinterpret_cast<uintptr_t>(x) % 16 != 0) return SA_ERR_SHAPE;
@@ -122,7 +123,8 @@ extern "C" sa_status sa_window_kv_update(uint16_t *ring, int64_t ring_stride, ui
 }
 
 static sa_status kv8_args(int64_t n_rows, int32_t row_len) {
-    if (n_rows < 0 || row_len <= 0 || row_len % 32 != 0) return SA_ERR_SHAPE;
+    if (n_rows < 0 || row_len <= 0 || row_len % 32 != 0 || !mul_le(n_rows, row_len / 8, 0x7fffffffLL * 256))
+        return SA_ERR_SHAPE;
     if (row_len > 32 * SA_KV8_SCALE_BYTES) return SA_ERR_UNSUPPORTED;
     return SA_OK;
 }

@@ -32,6 +32,8 @@ extern "C" sa_status sa_apply_rotary(uint16_t *x, int64_t b, int64_t s, int32_t 
                                      int32_t inverse, void *stream) {
     if (b < 0 || s < 0 || h < 0 || row_len < 0 || rope_dim < 0 || n_pos < 0 || start_pos < 0) return SA_ERR_SHAPE;
     if (rope_dim % 2 != 0 || rope_dim > row_len || row_len % 2 != 0) return SA_ERR_SHAPE;
+    if (!mul_le(b, s, 0x7fffffffLL) || !mul_le(b * s, (int64_t)h * (rope_dim / 2), 0x7fffffffLL * 256))
+        return SA_ERR_SHAPE;
     const int64_t n_pairs = b * s * h * (rope_dim / 2);
     if (n_pairs == 0) return SA_OK;
     if (!x || !table) return SA_ERR_NULL;

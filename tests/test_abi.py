@@ -132,3 +132,29 @@ def test_indexer_topk_argument_checks(lib):
     assert f(None, 1, 1, 10, 40, 4, 4, 0, None, 3, 0, None) == sa.SA_ERR_SHAPE      # row narrower than topk
     assert f(None, 0, 1, 10, 40, 4, 4, 0, None, 4, 0, None) == sa.SA_OK             # no rows
     assert f(None, 1, 1, 10, 40, 4, 4, 0, None, 4, 0, None) == sa.SA_ERR_NULL
+
+
+def test_sizes_past_the_supported_range_are_rejected(lib):
+    """Products of sizes that would overflow are refused with SA_ERR_SHAPE before
+    any pointer is looked at or anything is launched (null pointers here)."""
+    import sparse_latent_attention_02_amd as sa
+    big = 1 << 40
+    # (q, kv, sink, idx, b, s, h, d, rows, topk, scale, out, ws, ws_bytes, stream)
+    assert lib.sa_sparse_attn(None, None, None, None, big, big, 1, 64, 1, 1, 0.1, None, None, 0, None) == \
+        sa.SA_ERR_SHAPE
+    assert lib.sa_sparse_attn(None, None, None, None, 1 << 20, 1 << 12, 1, 64, 1, 1, 0.1, None, None, 0, None) == \
+        sa.SA_ERR_SHAPE                                                   # b * s past 2^31 - 1 queries
+    assert lib.sa_sparse_attn(None, None, None, None, big, 0, 1, 64, 1, 1, 0.1, None, None, 0, None) == sa.SA_OK
+    assert lib.sa_sparse_attn_workspace_bytes(big, big, 64, 512, 4096) == 0
+    assert lib.sa_sparse_attn_workspace_bytes_ex(big, big, 64, 512, 4096, 0, 4) == 0
+    assert lib.sa_sparse_attn_kv8_workspace_bytes(big, big, 64, 512, 4096, 4) == 0
+    # (x, n_rows, row_len, stream)
+    assert lib.sa_act_quant_fp8_inplace(None, 1 << 62, 512, None) == sa.SA_ERR_SHAPE
+    assert lib.sa_kv8_pack(None, None, None, 1 << 62, 512, None) == sa.SA_ERR_SHAPE
+    assert lib.sa_kv8_unpack(None, None, None, 1 << 62, 512, None) == sa.SA_ERR_SHAPE
+    # (x, b, s, h, row_len, rope_dim, table, n_pos, start_pos, inverse, stream)
+    assert lib.sa_apply_rotary(None, big, big, 1, 64, 16, None, 8, 0, 1, None) == sa.SA_ERR_SHAPE
+    # (idx, row_stride, col0, cidx, n_rows, kc, offset, stream)
+    assert lib.sa_append_compressed_idxs(None, 1 << 20, 0, None, 1 << 62, 1 << 20, 0, None) == sa.SA_ERR_SHAPE
+    # (window, bsz, seqlen, start_pos, idx, row_stride, stream)
+    assert lib.sa_window_topk_idxs(1 << 30, 1 << 30, 1 << 30, 0, None, 1 << 30, None) == sa.SA_ERR_SHAPE
