@@ -1480,6 +1480,14 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
             else
                 prep(t + 1, v_up, okm_nxt, src_nxt);
         }
+        // The entries three stages ahead are fetched here, not after the score
+        // product: a branch between the last score MFMA and the reads of its
+        // result hid that dependency from the compiler's wait-state insertion,
+        // and the reads came after fewer wait states than the matrix unit needs.
+        if (more) {
+            if (issue) v_up = v_after;  // (bf16 rows: shifted in the prologue for stage 0)
+            v_after = fetch_stage(t + 3);
+        }
         if (t == 0) {
             // Q as the B operand of the scores: lane (g, n) holds q[head n][32 ks + 8 g .. +8]
 #pragma unroll
@@ -1503,10 +1511,6 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
             }
             s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qreg[ks], s0, 0, 0, 0);
             s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qreg[ks + 1], s1, 0, 0, 0);
-        }
-        if (more) {
-            if (issue) v_up = v_after;  // (bf16 rows: shifted in the prologue for stage 0)
-            v_after = fetch_stage(t + 3);
         }
         // value i of lane (g, n): row RPW wave + 4 g + i, head n
         float sv[4];
