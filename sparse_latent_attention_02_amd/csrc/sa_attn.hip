@@ -1240,12 +1240,27 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
     const int32_t *dummy = reinterpret_cast<const int32_t *>(p.sink);
     auto fetch_stage = [&](int j) -> int {
         const int e = lo + j * C::ROWS + eoff;
-        if (FUSED) return e < hi ? step_entry(p, qi, e) : -1;
-        const int v = *(hi > lo ? idxq + min(e, hi - 1) : dummy);
-        return e < hi ? v : -1;
+        return e < hi ? step_entry(p, qi, e) : -1;
     };
-    // The first three stages' entries.  Index lists: the loads go out together
-    // inside one uniform branch, so one memory latency covers them.
+    // An index-list entry fetched ahead inside the stage loop is split into its
+    // load (load_entry, from a clamped address so that the load is unconditional)
+    // and its range check (finish_entry), done only at a later stage, after that
+    // stage's wait: a use right behind the load would make the compiler wait for
+    // it there, and that wait would also cover the row copies issued after it.
+    // (The fused step fetches its entries whole: its window entries are computed,
+    // not loaded, and splitting them measured slower there.)
+    auto load_entry = [&](int j) -> int {
+        if (FUSED) return fetch_stage(j);
+        const int e = lo + j * C::ROWS + eoff;
+        return *(hi > lo ? idxq + min(e, hi - 1) : dummy);
+    };
+    auto finish_entry = [&](int j, int v) -> int {
+        if (FUSED) return v;
+        return lo + j * C::ROWS + eoff < hi ? v : -1;
+    };
+    // The first three stages' entries (stage 2's loaded, not yet checked).  Index
+    // lists: the loads go out together inside one uniform branch, so one memory
+    // latency covers them.
     int v0, v_up, v_after;  // entries of stages 0, 1 (the next to copy), 2
     if (FUSED) {
         v0 = fetch_stage(0);
@@ -1261,7 +1276,7 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
         }
         v0 = e0 < hi ? a0 : -1;
         v_up = e1 < hi ? a1 : -1;
-        v_after = e2 < hi ? a2 : -1;
+        v_after = a2;
     }
     // the entries are in registers before any copy goes out: a compiler-placed wait
     // for them after the copies would also wait for the copies
@@ -1407,7 +1422,7 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
 #pragma unroll 1
                 for (int u = 0; u < C::RPW; ++u) copy_rows(1, okm_nxt, src_nxt, u, u + 1);
                 n_early = __builtin_popcount(okm_nxt);  // stage 1's copies (rows of -1 are zero-filled instead)
-                v_up = v_after;                          // entries of stage 2 (stage 3's are fetched later)
+                v_up = finish_entry(2, v_after);         // entries of stage 2 (stage 3's are fetched later)
             }
         }
     }
@@ -1480,13 +1495,13 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
             else
                 prep(t + 1, v_up, okm_nxt, src_nxt);
         }
-        // The entries three stages ahead are fetched here, not after the score
+        // The entries three stages ahead are loaded here, not after the score
         // product: a branch between the last score MFMA and the reads of its
         // result hid that dependency from the compiler's wait-state insertion,
         // and the reads came after fewer wait states than the matrix unit needs.
         if (more) {
-            if (issue) v_up = v_after;  // (bf16 rows: shifted in the prologue for stage 0)
-            v_after = fetch_stage(t + 3);
+            if (issue) v_up = finish_entry(t + 2, v_after);  // (bf16 rows: done in the prologue for stage 0)
+            v_after = load_entry(t + 3);
         }
         if (t == 0) {
             // Q as the B operand of the scores: lane (g, n) holds q[head n][32 ks + 8 g .. +8]
