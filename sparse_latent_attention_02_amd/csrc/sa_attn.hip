@@ -1182,9 +1182,10 @@ struct DecodeCfg {
     static constexpr int RPI8 = 64 / CPR8;
     static constexpr int NCI8 = RPW / RPI8;       // code copies per wave per stage (+1 for the scales)
     static constexpr int STG8 = ROWS * D + ROWS * 16;
-    static constexpr int XPT = ROWS * (D / 8) / THREADS;  // bf16 chunks each thread expands per stage
+    static constexpr int RPR = 64 / (D / 8);     // rows a wavefront expands per round (one chunk per lane)
+    static constexpr int XPW = RPW / RPR;         // expansion rounds per wavefront and stage (its own rows)
     static_assert(KS >= 2 && KS % 2 == 0 && DT >= 1 && RPW == 16, "tiling");
-    static_assert(NCI8 >= 1 && (D / 8) <= 64 && XPT >= 1, "kv8 tiling");
+    static_assert(NCI8 >= 1 && (D / 8) <= 64 && XPW >= 1 && XPW * RPR == RPW, "kv8 tiling");
 };
 
 template <int D, bool FUSED, bool KV8>
@@ -1197,6 +1198,7 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
     __shared__ float smax[C::NW][16];
     __shared__ float ssum[C::NW][16];
     __shared__ __attribute__((aligned(16))) float rtab[D];  // the query's rotation table row
+    __shared__ __attribute__((aligned(16))) char newbuf[KV8 && FUSED ? 2 * D : 16];  // kv8 step: the raw new row
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave values in SGPRs
@@ -1299,18 +1301,16 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
     const uint32_t q_base = lds_addr((const SA_LDS void *)qbuf);
     const SA_LDS char *lds = (const SA_LDS char *)smem;
 
-    // kv8 fused step: the new row never passes through the fp8 staging; the
-    // threads that expand its chunks (row r_new of stage st_new: expansion round
-    // k_new, wave w_conv, lanes from l_new) hold it raw from the start, round it
-    // through fp8 in registers and write both the bf16 values (into the stage) and
-    // the codes (into the ring, head group 0, at the end)
-    const int r_new = has_new ? w_new * C::RPW + u_new : 0;
-    const int k_new = (r_new * (D / 8)) / C::THREADS;
-    const int w_conv = ((r_new * (D / 8)) % C::THREADS) / 64;
-    const int l_new = (r_new * (D / 8)) % 64;
-    const bool holds_new = KV8 && has_new && wave == w_conv && lane >= l_new && lane < l_new + D / 8;
-    u32x4_t new_raw = {0u, 0u, 0u, 0u};
-    if (holds_new) new_raw = *reinterpret_cast<const u32x4_t *>(p.kv_new + (int64_t)qi * D + (lane - l_new) * 8);
+    // kv8 fused step: the new row never passes through the fp8 staging.  Wave
+    // w_new copies it raw into newbuf with its first copies (a direct copy like
+    // the others: a register load would get a wait of the compiler's own, which
+    // would also wait for every copy issued before its first use); the lanes that
+    // expand its chunks (row u_new of the wave's rows in stage st_new: expansion
+    // round k_new) read it there, round it through fp8 in registers and write both
+    // the bf16 values (into the stage) and the codes (into the ring, head group 0,
+    // at the end)
+    const int k_new = u_new / C::RPR;
+    const bool holds_new = KV8 && has_new && wave == w_new && lane / (D / 8) == u_new % C::RPR;
     u32x2_t new_codes = {0u, 0u};
     uint32_t new_sb = 127;
 
@@ -1404,6 +1404,9 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
             }
         }
         if constexpr (KV8) {
+            if (FUSED && has_new && wave == w_new && chunk_lane)
+                dma_16B(p.kv_new + (int64_t)qi * D + lane * 8,
+                        __builtin_amdgcn_readfirstlane(lds_addr((const SA_LDS void *)newbuf)));
             int rowv0;
             prep8(v0, okm_cur, rowv0);
 #pragma unroll 1
@@ -1445,7 +1448,6 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
             wait_vmcnt_upto16(n_early);
         else
             asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
-        if (KV8 && t == 0) asm volatile("" : : "v"(new_raw));  // (it was loaded before any copy)
         if (!KV8 && FUSED && t == st_new && wave == w_new) {
             // the raw new row has landed: round it through fp8 in place
             SA_LDS u32x4_t *nr = reinterpret_cast<SA_LDS u32x4_t *>((SA_LDS char *)stage +
@@ -1456,10 +1458,16 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
         }
         lds_barrier();  // every wave's rows (and the head rows) in place; stage t-1 fully consumed
         if constexpr (KV8) {
-            // ---- expand the stage's codes into the bf16 stage buffer ----
+            // ---- expand this wave's rows of the stage (the ones it copied) into the
+            //      bf16 stage buffer.  Its score product reads only these; the other
+            //      waves' rows are read (as V) after the barrier that publishes the
+            //      maxima, so no barrier is needed here. ----
             const SA_LDS char *s8 = (const SA_LDS char *)stg8 + (t & 1) * C::STG8;
             u32x4_t nb = {0u, 0u, 0u, 0u};
-            if (FUSED && has_new && t == st_new && wave == w_conv) {  // wave-uniform: every lane rounds
+            if (FUSED && has_new && t == st_new && wave == w_new) {  // wave-uniform: every lane rounds
+                const u32x4_t new_raw = holds_new ? *reinterpret_cast<const SA_LDS u32x4_t *>(
+                                                        (const SA_LDS char *)newbuf + 16 * (lane % (D / 8)))
+                                                  : u32x4_t{0u, 0u, 0u, 0u};
                 float e[8];
                 const float sc = fp8_block_round(new_raw, e);
 #pragma unroll
@@ -1471,9 +1479,8 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
                                     (e4m3_code(e[4 * jj + 2]) << 16) | (e4m3_code(e[4 * jj + 3]) << 24);
             }
 #pragma unroll
-            for (int k = 0; k < C::XPT; ++k) {
-                const int gch = k * C::THREADS + tid;
-                const int r = gch / (D / 8), c = gch % (D / 8);
+            for (int k = 0; k < C::XPW; ++k) {
+                const int r = C::RPW * wave + k * C::RPR + lane / (D / 8), c = lane % (D / 8);
                 u32x4_t o;
                 if (FUSED && holds_new && t == st_new && k == k_new) {
                     o = nb;
@@ -1484,7 +1491,6 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
                 }
                 *reinterpret_cast<SA_LDS u32x4_t *>((SA_LDS char *)smem + r * C::RS + 16 * c) = o;
             }
-            lds_barrier();
         }
         const bool more = t + 1 < nst;  // stage t+1 goes into the buffer stage t-1 used
         const bool issue = more && (KV8 || t > 0);  // (bf16 rows: stage 1 went out in the prologue)
@@ -1607,7 +1613,7 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
 
     if constexpr (KV8) {
         if (FUSED && hg == 0 && holds_new) {
-            const int c = lane - l_new;
+            const int c = lane % (D / 8);
             const int64_t rrow = (int64_t)bi * p.rows + p.new_slot;
             *reinterpret_cast<u32x2_t *>(p.kv8c_ring + rrow * D + 8 * c) = new_codes;
             if ((c & 3) == 0) p.kv8s_ring[rrow * 16 + c / 4] = (uint8_t)new_sb;
