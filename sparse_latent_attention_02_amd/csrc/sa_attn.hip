@@ -306,6 +306,34 @@ struct Compactor {
         }
     }
 
+    // the fused decode step's entries [c0, c1), built in place: ring slots by
+    // formula, compressed entries from cidx.  The compressed indices are loaded
+    // from clamped addresses, all of a thread's loads before any value is used:
+    // a load under a per-lane condition gets a wait of its own right behind it,
+    // which would put one memory latency per entry on the startup path.
+    __device__ __forceinline__ void load_step(const AttnParams &p, uint32_t qi, int c0, int c1) {
+        int c[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) c[k] = -1;
+        if (p.kc > 0) {  // (uniform)
+            const int32_t *crow = p.cidx + (int64_t)qi * p.kc;
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const int e = c0 + k * NT + (int)threadIdx.x;
+                c[k] = crow[min(max(e - p.window, 0), p.kc - 1)];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int e = c0 + k * NT + (int)threadIdx.x;
+            int slot = p.wbase + e;
+            if (slot >= p.window) slot -= p.window;
+            const int ring = (int64_t)slot <= p.pos ? slot : -1;
+            const int comp = c[k] < 0 ? -1 : (int)((uint32_t)c[k] + (uint32_t)p.window);
+            v[k] = e >= c1 ? -1 : (e < p.window ? ring : comp);
+        }
+    }
+
     // the raw entries of [c0, c1) from list[] (placed there by direct copies:
     // entry e at list[e - c0]); read before pack() rewrites list[]
     __device__ __forceinline__ void load_lds(const int *list, int c0, int c1) {
@@ -550,7 +578,10 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
         new_raw = *reinterpret_cast<const u32x4_t *>(p.kv_new + (int64_t)qi * D + lane * 8);
     // the first index chunk goes in flight before anything else: it heads the critical path
     Compactor<C::THREADS> cmp;
-    cmp.load(fetch, lo, min(hi, lo + kListCap));
+    if constexpr (FUSED)
+        cmp.load_step(p, qi, lo, min(hi, lo + kListCap));
+    else
+        cmp.load(fetch, lo, min(hi, lo + kListCap));
 
     cmp.ready();
     if (has_new && wave == 0) {
@@ -623,7 +654,12 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
     again = false;
     for (int c0 = lo; c0 < hi; c0 += kListCap) {
         const int c1 = min(hi, c0 + kListCap);
-        if (c0 != lo || !first_pass) cmp.load(fetch, c0, c1);
+        if (c0 != lo || !first_pass) {
+            if constexpr (FUSED)
+                cmp.load_step(p, qi, c0, c1);
+            else
+                cmp.load(fetch, c0, c1);
+        }
         if (FUSED && first_pass && hg == 0 && p.idx_out) cmp.store(p.idx_out + (int64_t)qi * p.topk, c0, c1);
         const int nv = cmp.pack(p.rows, list, wcnt);
         const int nst = (nv + C::ROWS - 1) / C::ROWS;
@@ -900,7 +936,6 @@ __global__ void __launch_bounds__(128, 2) sa_attn_pair(const AttnParams p) {
     const int lo = (int)sp * p.split_len;
     const int hi = min(p.topk, lo + p.split_len);
     const int32_t *idxq = FUSED ? nullptr : p.idx + (int64_t)qi * p.topk;
-    auto fetch = [&](int e) -> int { return FUSED ? step_entry(p, qi, e) : idxq[e]; };
     const bool has_new = FUSED && p.window - 1 >= lo && p.window - 1 < hi;
     u32x4_t new_raw = {0u, 0u, 0u, 0u};
     if (has_new && wave == 0 && chunk_lane)
@@ -919,7 +954,7 @@ __global__ void __launch_bounds__(128, 2) sa_attn_pair(const AttnParams p) {
             if (e0 + lane < c1) dma_4B(idxq + e0 + lane, list_base + (uint32_t)(e0 - c0) * 4);
     };
     if (FUSED)
-        cmp.load(fetch, lo, min(hi, lo + C::LIST_CAP));
+        cmp.load_step(p, qi, lo, min(hi, lo + C::LIST_CAP));
     else
         copy_idx(lo, min(hi, lo + C::LIST_CAP));
     const int head = ((int)hg * 2 + wave) * 32 + n;
@@ -978,7 +1013,7 @@ __global__ void __launch_bounds__(128, 2) sa_attn_pair(const AttnParams p) {
         const int c1 = min(hi, c0 + C::LIST_CAP);
         if (c0 != lo || !first_pass) {
             if (FUSED)
-                cmp.load(fetch, c0, c1);
+                cmp.load_step(p, qi, c0, c1);
             else
                 copy_idx(c0, c1);
         }
