@@ -1259,18 +1259,13 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
     const int head = (int)hg * C::HEADS + n;
     const bool head_ok = head < p.h;
     // the head's sink, loaded before any copy goes out (a load issued after them
-    // would wait behind them at the end).  Without the ring formula, every load
-    // here is unconditional, from a clamped address, with the value masked
-    // afterwards: a load inside a divergent branch gets a wait for it at the
-    // branch's end, which would put a memory latency on the startup path.  (The
-    // one-launch step keeps the conditional forms: measured faster there.)
-    float sink_h;
-    if (FUSED) {
-        sink_h = (head_ok && p.n_sp == 1) ? p.sink[head] : 0.0f;
-    } else {
-        const float sink_any = p.sink[min(head, p.h - 1)];
-        sink_h = (head_ok && p.n_sp == 1) ? sink_any : 0.0f;
-    }
+    // would wait behind them at the end), unconditionally from a clamped address
+    // with the value masked afterwards: under a per-lane condition the compiler
+    // put the scaling of the value right behind the load in the same branch, so
+    // the load's whole round trip stood before the first copy (fp8-resident step
+    // 2.3% slower, the bf16 one 1.1%)
+    const float sink_any = p.sink[min(head, p.h - 1)];
+    const float sink_h = (head_ok && p.n_sp == 1) ? sink_any : 0.0f;
     const bool rot = p.rope != nullptr && p.n_sp == 1 && nst > 0;
     const int eoff = C::RPW * wave + (lane & 15);
     // (a readable dummy for a load whose value is not needed: the sink)
