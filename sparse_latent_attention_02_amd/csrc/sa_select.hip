@@ -9,12 +9,12 @@
 // select over order-preserving 32-bit keys (digits of 12, 10 and 10 bits, most
 // significant first: a histogram of the keys that match the digits fixed so
 // far, then the digit where the count from the top reaches the number still to
-// take).  A
-// last pass over the row in position order keeps the keys above that threshold
-// and the first few equal to it, with a workgroup prefix sum giving each kept
-// position its output column -- so the output comes out in position order with
-// no sort.  Rows of up to kKeyCap positions keep their keys in LDS; longer rows
-// are re-read from memory in each pass.
+// take).  A last pass over the row in position order keeps the keys above that
+// threshold and the first few equal to it, with a workgroup prefix sum giving
+// each kept position its output column -- so the output comes out in position
+// order with no sort.  Rows of up to kKeyCap positions keep their keys in
+// registers (indexer_topk_kernel); longer rows are re-read from memory in each
+// pass (indexer_topk_stream_kernel).
 #include "sa_device.h"
 #include "../../include/sparse_attn.h"
 
@@ -23,8 +23,8 @@ namespace {
 using namespace sa;
 
 constexpr int kSelThreads = 1024;
-constexpr int kKeyCap = 16384;  // keys held in LDS (64 KiB)
-constexpr int kPerThread = 16;  // consecutive positions per thread in the ordered pass (kKeyCap / kSelThreads)
+constexpr int kKeyCap = 16384;  // keys held in registers: 16 per thread
+constexpr int kPerThread = 16;  // consecutive positions per thread in the streaming ordered pass
 constexpr int kMaxBins = 4096;  // the widest digit: 12 bits
 
 // f32 -> u32 with the same order (larger value, larger key); -inf is the
@@ -75,15 +75,213 @@ __device__ __forceinline__ uint32_t wg_inclusive_sum(uint32_t v, uint32_t *sums,
     return before + x;
 }
 
-template <bool CACHED>
-__global__ void __launch_bounds__(kSelThreads) indexer_topk_kernel(const float *__restrict__ scores, int64_t s,
+// The digit of the need-th largest key among those a histogram counted (nb
+// bins, bpt = nb / NT consecutive bins per thread, bins in thread
+// order) and the number of keys in the bins above that digit.  wsum[w] holds
+// the count of wavefront w's bins.  Every wavefront finds the digit by itself,
+// with no barrier: the wave totals name the wavefront whose bins hold it, and
+// that wavefront's per-lane counts, read again from the histogram, name the
+// lane and then the bin.
+template <int NT>
+__device__ __forceinline__ void find_digit(const uint32_t *hist, const uint32_t *wsum, int bpt, uint32_t need,
+                                           uint32_t &digit, uint32_t &above) {
+    constexpr int NW = NT / 64;
+    uint32_t tot[NW];
+#pragma unroll
+    for (int w = 0; w < NW; w += 4) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(wsum + w);
+        tot[w] = q.x, tot[w + 1] = q.y, tot[w + 2] = q.z, tot[w + 3] = q.w;
+    }
+    uint32_t acc = 0, above_w = 0;
+    int ws = 0;
+    bool found = false;
+#pragma unroll
+    for (int w = NW - 1; w >= 0; --w) {  // from the highest bins down
+        if (!found && acc + tot[w] >= need) {
+            found = true;
+            ws = w;
+            above_w = acc;
+        }
+        acc += tot[w];
+    }
+    const int lane = threadIdx.x & 63;
+    const int th = 64 * ws + lane;
+    uint32_t c = 0;
+    for (int j = 0; j < bpt; ++j) c += hist[th * bpt + j];
+    const uint32_t incl = wave_inclusive_sum(c);
+    uint32_t cum = above_w + (tot[ws] - incl);  // keys in the bins above this lane's
+    const bool hit = cum < need && cum + c >= need;
+    uint32_t d = (uint32_t)(th * bpt);
+    if (hit) {
+        for (int j = bpt - 1; j >= 0; --j) {
+            const uint32_t h = hist[th * bpt + j];
+            if (cum + h >= need) {
+                d = (uint32_t)(th * bpt + j);
+                break;
+            }
+            cum += h;
+        }
+    }
+    const uint64_t m = __builtin_amdgcn_ballot_w64(hit);
+    const int src = m ? __builtin_ctzll(m) : 0;
+    digit = (uint32_t)__builtin_amdgcn_readlane((int)d, src);
+    above = (uint32_t)__builtin_amdgcn_readlane((int)cum, src);
+}
+
+// Rows of up to kKeyCap positions, NT threads.  Thread tid holds the keys of
+// positions 4 (tid + NT i) + j, j < 4, i < TILES: each load is a 16-byte piece per lane,
+// consecutive across the lanes.  The three histograms are cleared once, up
+// front, so a pass needs two barriers (after its atomics, after its wave
+// totals); the ordered pass takes the same layout, tile by tile.
+template <int NT>
+__global__ void __launch_bounds__(NT) indexer_topk_kernel(const float *__restrict__ scores, int64_t s,
                                                                    int32_t T, int64_t start_pos, int32_t ratio,
                                                                    int32_t topk, int32_t offset,
                                                                    int32_t *__restrict__ out, int64_t row_stride,
                                                                    int32_t col0) {
-    // key t at word t + t / 16: a thread's 16 consecutive keys (the ordered pass)
-    // then sit in 16 different banks across the lanes of a read
-    __shared__ uint32_t keys[CACHED ? kKeyCap + kKeyCap / 16 : 1];
+    constexpr int NW = NT / 64;
+    constexpr int TILES = kKeyCap / (4 * NT);  // tiles of 4 NT positions, two to a count word
+    constexpr int HW = kMaxBins + 2 * 1024;     // the three digits' histograms
+    __shared__ __attribute__((aligned(16))) uint32_t hist[HW];
+    __shared__ __attribute__((aligned(16))) uint32_t wsum[3][NW < 4 ? 4 : NW];
+    __shared__ __attribute__((aligned(16))) uint32_t osum[NW][TILES];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t r = blockIdx.x;
+    const int64_t si = r % s;
+    const int64_t cl64 = start_pos == 0 ? (si + 1) / ratio : (start_pos + s) / ratio;  // compress_lens
+    const int cl = (int)(cl64 < T ? cl64 : (int64_t)T);  // positions past the row are never read
+    const float *sr = scores + r * T;
+    int32_t *orow = out + r * row_stride + col0;
+
+    if (topk >= T) {  // every position is taken
+        for (int t = tid; t < T; t += NT) orow[t] = t < cl ? t + offset : -1;
+        return;
+    }
+    // every load of the row in flight at once
+    float v[4 * TILES];
+    const bool vec = (T & 3) == 0 && ((uintptr_t)scores & 15) == 0;
+#pragma unroll
+    for (int i = 0; i < TILES; ++i) {
+        const int p = 4 * (tid + NT * i);
+        if (vec) {
+            const float4 q = p < T ? *reinterpret_cast<const float4 *>(sr + p) : float4{0.f, 0.f, 0.f, 0.f};
+            v[4 * i] = q.x, v[4 * i + 1] = q.y, v[4 * i + 2] = q.z, v[4 * i + 3] = q.w;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[4 * i + j] = p + j < T ? sr[p + j] : 0.0f;
+        }
+    }
+    // the histograms cleared while the loads are in flight
+    for (int i = tid; i < HW / 4; i += NT) reinterpret_cast<uint4 *>(hist)[i] = uint4{0u, 0u, 0u, 0u};
+    // Positions past the row end take key 0, below every score's key (-inf's is
+    // the smallest): they land in the lowest bins, under the topk < T keys of
+    // the row, so the threshold is a key of the row and they are never taken.
+    uint32_t k[4 * TILES];
+#pragma unroll
+    for (int i = 0; i < TILES; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int p = 4 * (tid + NT * i) + j;
+            const uint32_t kv = order_key(v[4 * i + j]);
+            k[4 * i + j] = p < T ? (p < cl ? kv : kKeyNegInf) : 0u;
+        }
+    lds_barrier();
+
+    // ---- radix select of the threshold key (the topk-th largest): digits of
+    //      12, 10 and 10 bits, most significant first.  The wide first digit
+    //      (sign, exponent, 3 mantissa bits) spreads scores that share a few
+    //      binades over many bins, so the histogram atomics rarely collide; the
+    //      later digits only count the few keys still matching. ----
+    uint32_t prefix = 0, pmask = 0;
+    uint32_t need = (uint32_t)topk;  // how many keys matching the prefix are still to take
+#pragma unroll
+    for (int pass = 0; pass < 3; ++pass) {
+        const int width = pass == 0 ? 12 : 10;
+        const int shift = pass == 0 ? 20 : (pass == 1 ? 10 : 0);
+        const int nb = 1 << width, bpt = nb / NT;
+        const uint32_t dmask = (uint32_t)nb - 1u;
+        uint32_t *h = hist + (pass == 0 ? 0 : kMaxBins + 1024 * (pass - 1));
+#pragma unroll
+        for (int q = 0; q < 4 * TILES; ++q)
+            if ((k[q] & pmask) == prefix) atomicAdd(&h[(k[q] >> shift) & dmask], 1u);
+        lds_barrier();
+        uint32_t c = 0;
+        for (int j = 0; j < bpt; ++j) c += h[tid * bpt + j];
+        const uint32_t x = wave_inclusive_sum(c);
+        if (lane == 63) wsum[pass][wave] = x;
+        lds_barrier();
+        uint32_t digit, above;
+        find_digit<NT>(h, wsum[pass], bpt, need, digit, above);
+        prefix |= digit << shift;
+        pmask |= dmask << shift;
+        need -= above;
+    }
+    const uint32_t thr = prefix;  // keys above are all taken, `need` of those equal to it
+
+    // ---- ordered pass: per tile, the keys above the threshold and those equal
+    //      to it, counted two tiles to a word (16-bit fields: a tile holds
+    //      4 NT positions): words [0, TILES / 2) the keys above, the rest the
+    //      equal ones ----
+    uint32_t cnt[TILES] = {};
+#pragma unroll
+    for (int i = 0; i < TILES; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int q = 4 * i + j;
+            const uint32_t f = 1u << (16 * (i & 1));
+            cnt[i >> 1] += k[q] > thr ? f : 0u;
+            cnt[TILES / 2 + (i >> 1)] += k[q] == thr ? f : 0u;
+        }
+    uint32_t excl[TILES];
+#pragma unroll
+    for (int w = 0; w < TILES; ++w) {
+        excl[w] = wave_inclusive_sum(cnt[w]) - cnt[w];
+        if (lane == 63) osum[wave][w] = excl[w] + cnt[w];
+    }
+    lds_barrier();
+    uint32_t before[TILES] = {}, total[TILES] = {};
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int f = 0; f < TILES; ++f) {
+            const uint32_t o = osum[w][f];
+            before[f] += w < wave ? o : 0u;
+            total[f] += o;
+        }
+    // compress_lens again, opaque to the compiler: otherwise it keeps the 16 lane
+    // masks of the key step alive across the passes for the test below
+    int cl_out = cl;
+    asm volatile("" : "+s"(cl_out));
+    uint32_t gt_tiles = 0, eq_tiles = 0;  // keys of each kind in the tiles before
+#pragma unroll
+    for (int i = 0; i < TILES; ++i) {
+        const int f = i >> 1, sh = 16 * (i & 1);
+        const uint32_t gt_before = gt_tiles + (((before[f] + excl[f]) >> sh) & 0xffffu);
+        const uint32_t eq_before = eq_tiles + (((before[TILES / 2 + f] + excl[TILES / 2 + f]) >> sh) & 0xffffu);
+        // equal keys are taken in position order while their rank among the
+        // equal keys is below need
+        uint32_t pos = gt_before + min(eq_before, need);
+        uint32_t eq_rank = eq_before;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int q = 4 * i + j;
+            const int t = 4 * (tid + NT * i) + j;
+            bool take = k[q] > thr;
+            if (k[q] == thr) take = eq_rank++ < need;
+            if (take && pos < (uint32_t)topk) orow[pos++] = t < cl_out ? t + offset : -1;
+        }
+        gt_tiles += (total[f] >> sh) & 0xffffu;
+        eq_tiles += (total[TILES / 2 + f] >> sh) & 0xffffu;
+    }
+}
+
+// Rows longer than kKeyCap: every pass reads the row's scores from memory.
+__global__ void __launch_bounds__(kSelThreads) indexer_topk_stream_kernel(const float *__restrict__ scores, int64_t s,
+                                                                   int32_t T, int64_t start_pos, int32_t ratio,
+                                                                   int32_t topk, int32_t offset,
+                                                                   int32_t *__restrict__ out, int64_t row_stride,
+                                                                   int32_t col0) {
     __shared__ uint32_t hist[kMaxBins];
     __shared__ uint32_t sums[kSelThreads / 64];
     __shared__ uint32_t pick[2];  // digit, count of matching keys above it
@@ -94,31 +292,12 @@ __global__ void __launch_bounds__(kSelThreads) indexer_topk_kernel(const float *
     const int64_t cl = start_pos == 0 ? (si + 1) / ratio : (start_pos + s) / ratio;  // compress_lens
     const float *sr = scores + r * T;
     int32_t *orow = out + r * row_stride + col0;
-    auto key_of = [&](int t) -> uint32_t {
-        if (CACHED) return keys[t + (t >> 4)];
-        return t < cl ? order_key(sr[t]) : kKeyNegInf;
-    };
+    auto key_of = [&](int t) -> uint32_t { return t < cl ? order_key(sr[t]) : kKeyNegInf; };
 
     if (topk >= T) {  // every position is taken
         for (int t = tid; t < T; t += kSelThreads) orow[t] = t < cl ? t + offset : -1;
         return;
     }
-    if (CACHED) {
-        // every load of the row in flight at once, then the keys into LDS
-        constexpr int KPT = kKeyCap / kSelThreads;
-        float v[KPT];
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int t = tid + i * kSelThreads;
-            v[i] = t < T ? sr[t] : 0.0f;
-        }
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int t = tid + i * kSelThreads;
-            if (t < T) keys[t + (t >> 4)] = t < cl ? order_key(v[i]) : kKeyNegInf;
-        }
-    }
-
     // ---- radix select of the threshold key (the topk-th largest): digits of
     //      12, 10 and 10 bits, most significant first.  The wide first digit
     //      (sign, exponent, 3 mantissa bits) spreads scores that share a few
@@ -219,11 +398,11 @@ extern "C" sa_status sa_indexer_topk(const float *scores, int64_t b, int64_t s, 
     if (!scores || !idx) return SA_ERR_NULL;
     if (rows > 0x7fffffffLL) return SA_ERR_SHAPE;
     if (n_cols <= kKeyCap)
-        hipLaunchKernelGGL(indexer_topk_kernel<true>, dim3((unsigned)rows), dim3(kSelThreads), 0,
-                           (hipStream_t)stream, scores, s, n_cols, start_pos, ratio, topk, offset, idx, row_stride,
-                           col0);
+        hipLaunchKernelGGL(indexer_topk_kernel<kSelThreads>, dim3((unsigned)rows), dim3(kSelThreads), 0,
+                           (hipStream_t)stream,
+                           scores, s, n_cols, start_pos, ratio, topk, offset, idx, row_stride, col0);
     else
-        hipLaunchKernelGGL(indexer_topk_kernel<false>, dim3((unsigned)rows), dim3(kSelThreads), 0,
+        hipLaunchKernelGGL(indexer_topk_stream_kernel, dim3((unsigned)rows), dim3(kSelThreads), 0,
                            (hipStream_t)stream, scores, s, n_cols, start_pos, ratio, topk, offset, idx, row_stride,
                            col0);
     return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
