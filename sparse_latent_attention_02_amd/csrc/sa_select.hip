@@ -75,52 +75,59 @@ __device__ __forceinline__ uint32_t wg_inclusive_sum(uint32_t v, uint32_t *sums,
     return before + x;
 }
 
-// The digit of the need-th largest key among those a histogram counted (nb
-// bins, bpt = nb / NT consecutive bins per thread, bins in thread
-// order) and the number of keys in the bins above that digit.  wsum[w] holds
-// the count of wavefront w's bins.  Every wavefront finds the digit by itself,
-// with no barrier: the wave totals name the wavefront whose bins hold it, and
-// that wavefront's per-lane counts, read again from the histogram, name the
-// lane and then the bin.
-template <int NT>
-__device__ __forceinline__ void find_digit(const uint32_t *hist, const uint32_t *wsum, int bpt, uint32_t need,
+// Inclusive prefix sum over each row of 16 lanes (DPP row shifts by 1, 2, 4, 8).
+__device__ __forceinline__ uint32_t row_inclusive_sum(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    return x;
+}
+
+// The digit of the need-th largest key among those a histogram counted (BPT
+// consecutive bins per thread, bins in thread order) and the number of keys in
+// the bins above that digit.  wsum[w] holds the count of wavefront w's bins.
+// Every wavefront finds the digit by itself, with no barrier and no loop over
+// the wavefronts: lane l < NW takes wavefront NW - 1 - l's total, so the lanes'
+// prefix sum counts from the highest bins down and a ballot names the
+// wavefront whose bins hold the digit; that wavefront's bins, read again from
+// the histogram, name the lane and then the bin.
+template <int NT, int BPT>
+__device__ __forceinline__ void find_digit(const uint32_t *hist, const uint32_t *wsum, uint32_t need,
                                            uint32_t &digit, uint32_t &above) {
     constexpr int NW = NT / 64;
-    uint32_t tot[NW];
-#pragma unroll
-    for (int w = 0; w < NW; w += 4) {
-        const uint4 q = *reinterpret_cast<const uint4 *>(wsum + w);
-        tot[w] = q.x, tot[w + 1] = q.y, tot[w + 2] = q.z, tot[w + 3] = q.w;
-    }
-    uint32_t acc = 0, above_w = 0;
-    int ws = 0;
-    bool found = false;
-#pragma unroll
-    for (int w = NW - 1; w >= 0; --w) {  // from the highest bins down
-        if (!found && acc + tot[w] >= need) {
-            found = true;
-            ws = w;
-            above_w = acc;
-        }
-        acc += tot[w];
-    }
+    static_assert(NW <= 16, "the wave totals are scanned within one row of 16 lanes");
     const int lane = threadIdx.x & 63;
+    const uint32_t wt = lane < NW ? wsum[NW - 1 - lane] : 0u;
+    const uint32_t top = row_inclusive_sum(wt);  // lanes < NW: keys in wavefronts NW - 1 - lane and above
+    const uint64_t mw = __builtin_amdgcn_ballot_w64(lane < NW && top >= need);
+    const int lw = mw ? __builtin_ctzll(mw) : NW - 1;
+    const int ws = NW - 1 - lw;
+    const uint32_t above_w = (uint32_t)__builtin_amdgcn_readlane((int)(top - wt), lw);
+    const uint32_t tot_ws = (uint32_t)__builtin_amdgcn_readlane((int)wt, lw);
     const int th = 64 * ws + lane;
+    uint32_t bins[BPT];
+    if constexpr (BPT == 4) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(hist + 4 * th);
+        bins[0] = q.x, bins[1] = q.y, bins[2] = q.z, bins[3] = q.w;
+    } else {
+#pragma unroll
+        for (int j = 0; j < BPT; ++j) bins[j] = hist[th * BPT + j];
+    }
     uint32_t c = 0;
-    for (int j = 0; j < bpt; ++j) c += hist[th * bpt + j];
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) c += bins[j];
     const uint32_t incl = wave_inclusive_sum(c);
-    uint32_t cum = above_w + (tot[ws] - incl);  // keys in the bins above this lane's
+    uint32_t cum = above_w + (tot_ws - incl);  // keys in the bins above this lane's
     const bool hit = cum < need && cum + c >= need;
-    uint32_t d = (uint32_t)(th * bpt);
-    if (hit) {
-        for (int j = bpt - 1; j >= 0; --j) {
-            const uint32_t h = hist[th * bpt + j];
-            if (cum + h >= need) {
-                d = (uint32_t)(th * bpt + j);
-                break;
-            }
-            cum += h;
-        }
+    uint32_t d = (uint32_t)(th * BPT);
+    bool done = false;
+#pragma unroll
+    for (int j = BPT - 1; j >= 0; --j) {
+        const bool here = !done && cum + bins[j] >= need;
+        d = here ? (uint32_t)(th * BPT + j) : d;
+        cum += (!done && !here) ? bins[j] : 0u;
+        done = done || here;
     }
     const uint64_t m = __builtin_amdgcn_ballot_w64(hit);
     const int src = m ? __builtin_ctzll(m) : 0;
@@ -132,8 +139,9 @@ __device__ __forceinline__ void find_digit(const uint32_t *hist, const uint32_t 
 // positions 4 (tid + NT i) + j, j < 4, i < TILES: each load is a 16-byte piece per lane,
 // consecutive across the lanes.  The three histograms are cleared once, up
 // front, so a pass needs two barriers (after its atomics, after its wave
-// totals); the ordered pass takes the same layout, tile by tile.
-template <int NT>
+// totals); the first digit's atomics follow the loads tile by tile.  The
+// ordered pass takes the same layout, tile by tile.
+template <int NT, bool VEC>
 __global__ void __launch_bounds__(NT) indexer_topk_kernel(const float *__restrict__ scores, int64_t s,
                                                                    int32_t T, int64_t start_pos, int32_t ratio,
                                                                    int32_t topk, int32_t offset,
@@ -158,22 +166,26 @@ __global__ void __launch_bounds__(NT) indexer_topk_kernel(const float *__restric
         for (int t = tid; t < T; t += NT) orow[t] = t < cl ? t + offset : -1;
         return;
     }
-    // every load of the row in flight at once
+    // every load of the row in flight at once (VEC: T a multiple of 4 and the
+    // scores 16-byte aligned, so each piece is one load), unconditional, from a
+    // position clamped into the row (T > topk >= 1): a branch around them would
+    // make the first use wait for all of them
     float v[4 * TILES];
-    const bool vec = (T & 3) == 0 && ((uintptr_t)scores & 15) == 0;
 #pragma unroll
     for (int i = 0; i < TILES; ++i) {
         const int p = 4 * (tid + NT * i);
-        if (vec) {
-            const float4 q = p < T ? *reinterpret_cast<const float4 *>(sr + p) : float4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (VEC) {
+            const float4 q = *reinterpret_cast<const float4 *>(sr + min(p, T - 4));
             v[4 * i] = q.x, v[4 * i + 1] = q.y, v[4 * i + 2] = q.z, v[4 * i + 3] = q.w;
         } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) v[4 * i + j] = p + j < T ? sr[p + j] : 0.0f;
+            for (int j = 0; j < 4; ++j) v[4 * i + j] = sr[min(p + j, T - 1)];
         }
     }
     // the histograms cleared while the loads are in flight
+#pragma unroll
     for (int i = tid; i < HW / 4; i += NT) reinterpret_cast<uint4 *>(hist)[i] = uint4{0u, 0u, 0u, 0u};
+    lds_barrier();
     // Positions past the row end take key 0, below every score's key (-inf's is
     // the smallest): they land in the lowest bins, under the topk < T keys of
     // the row, so the threshold is a key of the row and they are never taken.
@@ -185,8 +197,8 @@ __global__ void __launch_bounds__(NT) indexer_topk_kernel(const float *__restric
             const int p = 4 * (tid + NT * i) + j;
             const uint32_t kv = order_key(v[4 * i + j]);
             k[4 * i + j] = p < T ? (p < cl ? kv : kKeyNegInf) : 0u;
+            atomicAdd(&hist[k[4 * i + j] >> 20], 1u);  // the first digit
         }
-    lds_barrier();
 
     // ---- radix select of the threshold key (the topk-th largest): digits of
     //      12, 10 and 10 bits, most significant first.  The wide first digit
@@ -199,12 +211,16 @@ __global__ void __launch_bounds__(NT) indexer_topk_kernel(const float *__restric
     for (int pass = 0; pass < 3; ++pass) {
         const int width = pass == 0 ? 12 : 10;
         const int shift = pass == 0 ? 20 : (pass == 1 ? 10 : 0);
-        const int nb = 1 << width, bpt = nb / NT;
+        const int nb = 1 << width;
+        constexpr int bpt0 = kMaxBins / NT, bpt1 = 1024 / NT;
+        const int bpt = pass == 0 ? bpt0 : bpt1;
         const uint32_t dmask = (uint32_t)nb - 1u;
         uint32_t *h = hist + (pass == 0 ? 0 : kMaxBins + 1024 * (pass - 1));
+        if (pass > 0) {
 #pragma unroll
-        for (int q = 0; q < 4 * TILES; ++q)
-            if ((k[q] & pmask) == prefix) atomicAdd(&h[(k[q] >> shift) & dmask], 1u);
+            for (int q = 0; q < 4 * TILES; ++q)
+                if ((k[q] & pmask) == prefix) atomicAdd(&h[(k[q] >> shift) & dmask], 1u);
+        }
         lds_barrier();
         uint32_t c = 0;
         for (int j = 0; j < bpt; ++j) c += h[tid * bpt + j];
@@ -212,7 +228,10 @@ __global__ void __launch_bounds__(NT) indexer_topk_kernel(const float *__restric
         if (lane == 63) wsum[pass][wave] = x;
         lds_barrier();
         uint32_t digit, above;
-        find_digit<NT>(h, wsum[pass], bpt, need, digit, above);
+        if (pass == 0)
+            find_digit<NT, bpt0>(h, wsum[pass], need, digit, above);
+        else
+            find_digit<NT, bpt1>(h, wsum[pass], need, digit, above);
         prefix |= digit << shift;
         pmask |= dmask << shift;
         need -= above;
@@ -240,15 +259,17 @@ __global__ void __launch_bounds__(NT) indexer_topk_kernel(const float *__restric
         if (lane == 63) osum[wave][w] = excl[w] + cnt[w];
     }
     lds_barrier();
-    uint32_t before[TILES] = {}, total[TILES] = {};
+    // the wavefronts' totals: lane l < NW takes wavefront l's, a prefix sum over
+    // the lanes gives the counts before this wavefront and the tiles' totals
+    uint32_t before[TILES], total[TILES];
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
-    for (int w = 0; w < NW; ++w)
-#pragma unroll
-        for (int f = 0; f < TILES; ++f) {
-            const uint32_t o = osum[w][f];
-            before[f] += w < wave ? o : 0u;
-            total[f] += o;
-        }
+    for (int f = 0; f < TILES; ++f) {
+        const uint32_t o = lane < NW ? osum[lane][f] : 0u;
+        const uint32_t incl = row_inclusive_sum(o);
+        before[f] = (uint32_t)__builtin_amdgcn_readlane((int)(incl - o), wave_u);
+        total[f] = (uint32_t)__builtin_amdgcn_readlane((int)incl, NW - 1);
+    }
     // compress_lens again, opaque to the compiler: otherwise it keeps the 16 lane
     // masks of the key step alive across the passes for the test below
     int cl_out = cl;
@@ -397,10 +418,14 @@ extern "C" sa_status sa_indexer_topk(const float *scores, int64_t b, int64_t s, 
     if (rows == 0 || topk == 0) return SA_OK;
     if (!scores || !idx) return SA_ERR_NULL;
     if (rows > 0x7fffffffLL) return SA_ERR_SHAPE;
-    if (n_cols <= kKeyCap)
-        hipLaunchKernelGGL(indexer_topk_kernel<kSelThreads>, dim3((unsigned)rows), dim3(kSelThreads), 0,
-                           (hipStream_t)stream,
-                           scores, s, n_cols, start_pos, ratio, topk, offset, idx, row_stride, col0);
+    if (n_cols <= kKeyCap && (n_cols & 3) == 0 && ((uintptr_t)scores & 15) == 0)
+        hipLaunchKernelGGL((indexer_topk_kernel<kSelThreads, true>), dim3((unsigned)rows), dim3(kSelThreads), 0,
+                           (hipStream_t)stream, scores, s, n_cols, start_pos, ratio, topk, offset, idx, row_stride,
+                           col0);
+    else if (n_cols <= kKeyCap)
+        hipLaunchKernelGGL((indexer_topk_kernel<kSelThreads, false>), dim3((unsigned)rows), dim3(kSelThreads), 0,
+                           (hipStream_t)stream, scores, s, n_cols, start_pos, ratio, topk, offset, idx, row_stride,
+                           col0);
     else
         hipLaunchKernelGGL(indexer_topk_stream_kernel, dim3((unsigned)rows), dim3(kSelThreads), 0,
                            (hipStream_t)stream, scores, s, n_cols, start_pos, ratio, topk, offset, idx, row_stride,
