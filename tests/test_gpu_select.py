@@ -37,6 +37,9 @@ CASES = [
     (10, 1, 2048, 0, 4, 200, 2048, "zeros"),       # prefill: the same, under the causal mask
     (11, 8, 1, 65535, 4, 2048, 128, "relu"),       # decode: ReLU scores times signed weights (many -0)
     (12, 2, 1, 131071, 4, 2048, 128, "zeros"),     # decode: rows re-read from memory, signed zeros
+    (13, 6, 1, 40000, 3, 1500, 128, "normal"),     # decode: 13333 positions (odd: element loads, all tiles)
+    (14, 4, 1, 65536, 4, 2048, 128, "normal"),     # decode: T = 16384, the register form's cap
+    (15, 3, 1, 65539, 4, 3000, 128, "normal"),     # decode: T = 16385, one past the cap (streaming form)
 ]
 
 
@@ -74,6 +77,21 @@ def test_indexer_topk_vs_oracle(case):
     got = sa.indexer_topk(sc.to(DEV), start_pos, ratio, index_topk, offset)
     torch.cuda.synchronize()
     assert np.array_equal(got.cpu().numpy(), ref)
+
+
+def test_indexer_topk_misaligned_scores():
+    """Rows whose length is a multiple of 4 but whose base is not 16-byte aligned
+    take the element-load form."""
+    b, s, start_pos, ratio, topk = 5, 1, 40959, 4, 1024
+    T = (start_pos + s) // ratio
+    sc = make_scores(16, b, s, T, "normal")
+    flat = torch.empty(b * s * T + 1, dtype=torch.float32, device=DEV)
+    view = flat[1:].view(b, s, T)
+    view.copy_(sc.to(DEV))
+    assert view.data_ptr() % 16 != 0 and T % 4 == 0
+    got = sa.indexer_topk(view, start_pos, ratio, topk, 128)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), oracle.indexer_topk(sc.numpy(), start_pos, ratio, topk, 128))
 
 
 def test_indexer_topk_into_the_compressed_columns():
