@@ -13,8 +13,7 @@
 // threshold and the first few equal to it, with a workgroup prefix sum giving
 // each kept position its output column -- so the output comes out in position
 // order with no sort.  Rows of up to kKeyCap positions keep their keys in
-// registers (indexer_topk_kernel); longer rows are re-read from memory in each
-// pass (indexer_topk_stream_kernel).
+// registers; longer rows are read again, chunk by chunk, in each pass.
 #include "sa_device.h"
 #include "../../include/sparse_attn.h"
 
@@ -23,8 +22,7 @@ namespace {
 using namespace sa;
 
 constexpr int kSelThreads = 1024;
-constexpr int kKeyCap = 16384;  // keys held in registers: 16 per thread
-constexpr int kPerThread = 16;  // consecutive positions per thread in the streaming ordered pass
+constexpr int kKeyCap = 16384;  // positions per chunk: 16 keys per thread in registers
 constexpr int kMaxBins = 4096;  // the widest digit: 12 bits
 
 // f32 -> u32 with the same order (larger value, larger key); -inf is the
@@ -53,26 +51,6 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
     const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
     const int row = (threadIdx.x & 63) >> 4;
     return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
-}
-
-// Inclusive prefix sum over the workgroup of v (each thread's value, in thread
-// order); the total goes to *total.  Uses sums[kSelThreads / 64] in LDS; all
-// threads call it.
-__device__ __forceinline__ uint32_t wg_inclusive_sum(uint32_t v, uint32_t *sums, uint32_t *total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint32_t x = wave_inclusive_sum(v);
-    if (lane == 63) sums[wave] = x;
-    __syncthreads();
-    uint32_t before = 0, all = 0;
-#pragma unroll
-    for (int w = 0; w < kSelThreads / 64; ++w) {
-        const uint32_t sw = sums[w];
-        before += w < wave ? sw : 0u;
-        all += sw;
-    }
-    *total = all;
-    __syncthreads();  // sums may be reused by the next call
-    return before + x;
 }
 
 // Inclusive prefix sum over each row of 16 lanes (DPP row shifts by 1, 2, 4, 8).
@@ -135,24 +113,29 @@ __device__ __forceinline__ void find_digit(const uint32_t *hist, const uint32_t 
     above = (uint32_t)__builtin_amdgcn_readlane((int)cum, src);
 }
 
-// Rows of up to kKeyCap positions, NT threads.  Thread tid holds the keys of
-// positions 4 (tid + NT i) + j, j < 4, i < TILES: each load is a 16-byte piece per lane,
-// consecutive across the lanes.  The three histograms are cleared once, up
-// front, so a pass needs two barriers (after its atomics, after its wave
-// totals); the first digit's atomics follow the loads tile by tile.  The
-// ordered pass takes the same layout, tile by tile.
-template <int NT, bool VEC>
+// One row per workgroup of NT threads, taken in chunks of kKeyCap positions:
+// thread tid holds the keys of positions 4 (tid + NT i) + j of a chunk, j < 4,
+// i < TILES, so each load is a 16-byte piece per lane, consecutive across the
+// lanes.  A row of up to kKeyCap positions (STREAM false) is loaded once and
+// its keys stay in registers; a longer row (STREAM) is read again, chunk by
+// chunk, in every pass, the next chunk's loads in flight while the current one
+// is counted.  The three histograms are cleared once, up front, so a pass needs
+// two barriers (after its atomics, after its wave totals); the first digit's
+// atomics follow the loads tile by tile.  The ordered pass takes the same
+// layout, tile by tile, with one barrier per chunk.
+template <int NT, bool VEC, bool STREAM>
 __global__ void __launch_bounds__(NT) indexer_topk_kernel(const float *__restrict__ scores, int64_t s,
-                                                                   int32_t T, int64_t start_pos, int32_t ratio,
-                                                                   int32_t topk, int32_t offset,
-                                                                   int32_t *__restrict__ out, int64_t row_stride,
-                                                                   int32_t col0) {
+                                                          int32_t T, int64_t start_pos, int32_t ratio,
+                                                          int32_t topk, int32_t offset,
+                                                          int32_t *__restrict__ out, int64_t row_stride,
+                                                          int32_t col0) {
     constexpr int NW = NT / 64;
     constexpr int TILES = kKeyCap / (4 * NT);  // tiles of 4 NT positions, two to a count word
+    constexpr int KPT = 4 * TILES;             // keys per thread and chunk
     constexpr int HW = kMaxBins + 2 * 1024;     // the three digits' histograms
     __shared__ __attribute__((aligned(16))) uint32_t hist[HW];
     __shared__ __attribute__((aligned(16))) uint32_t wsum[3][NW < 4 ? 4 : NW];
-    __shared__ __attribute__((aligned(16))) uint32_t osum[NW][TILES];
+    __shared__ __attribute__((aligned(16))) uint32_t osum[STREAM ? 2 : 1][NW][TILES];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t r = blockIdx.x;
@@ -166,39 +149,51 @@ __global__ void __launch_bounds__(NT) indexer_topk_kernel(const float *__restric
         for (int t = tid; t < T; t += NT) orow[t] = t < cl ? t + offset : -1;
         return;
     }
-    // every load of the row in flight at once (VEC: T a multiple of 4 and the
-    // scores 16-byte aligned, so each piece is one load), unconditional, from a
-    // position clamped into the row (T > topk >= 1): a branch around them would
-    // make the first use wait for all of them
-    float v[4 * TILES];
+    const int nchunks = STREAM ? (T + kKeyCap - 1) / kKeyCap : 1;
+
+    // The loads of chunk c: unconditional, from positions clamped into the row
+    // (T > topk >= 1), since a branch around them would make the first use wait
+    // for all of them (VEC: T a multiple of 4 and the scores 16-byte aligned, so
+    // each piece is one load).
+    float v[KPT];
+    auto issue = [&](int c) {
+        const int base = c * kKeyCap;
 #pragma unroll
-    for (int i = 0; i < TILES; ++i) {
-        const int p = 4 * (tid + NT * i);
-        if constexpr (VEC) {
-            const float4 q = *reinterpret_cast<const float4 *>(sr + min(p, T - 4));
-            v[4 * i] = q.x, v[4 * i + 1] = q.y, v[4 * i + 2] = q.z, v[4 * i + 3] = q.w;
-        } else {
+        for (int i = 0; i < TILES; ++i) {
+            const int p = base + 4 * (tid + NT * i);
+            if constexpr (VEC) {
+                const float4 q = *reinterpret_cast<const float4 *>(sr + min(p, T - 4));
+                v[4 * i] = q.x, v[4 * i + 1] = q.y, v[4 * i + 2] = q.z, v[4 * i + 3] = q.w;
+            } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) v[4 * i + j] = sr[min(p + j, T - 1)];
+                for (int j = 0; j < 4; ++j) v[4 * i + j] = sr[min(p + j, T - 1)];
+            }
         }
-    }
+    };
+    // Positions past the row end take key 0, below every score's key (-inf's is
+    // the smallest): they land in the lowest bins, under the topk < T keys of
+    // the row, so the threshold is a key of the row and they are never taken.
+    uint32_t k[KPT];
+    auto key = [&](int c, int i, int j) {
+        const int p = c * kKeyCap + 4 * (tid + NT * i) + j;
+        const uint32_t kv = order_key(v[4 * i + j]);
+        k[4 * i + j] = p < T ? (p < cl ? kv : kKeyNegInf) : 0u;
+    };
+    // STREAM: the keys of chunk c, then the loads of the chunk after it (chunk 0
+    // after the last: the next pass starts there)
+    auto next_chunk = [&](int c) {
+#pragma unroll
+        for (int i = 0; i < TILES; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) key(c, i, j);
+        issue(c + 1 < nchunks ? c + 1 : 0);
+    };
+
+    issue(0);
     // the histograms cleared while the loads are in flight
 #pragma unroll
     for (int i = tid; i < HW / 4; i += NT) reinterpret_cast<uint4 *>(hist)[i] = uint4{0u, 0u, 0u, 0u};
     lds_barrier();
-    // Positions past the row end take key 0, below every score's key (-inf's is
-    // the smallest): they land in the lowest bins, under the topk < T keys of
-    // the row, so the threshold is a key of the row and they are never taken.
-    uint32_t k[4 * TILES];
-#pragma unroll
-    for (int i = 0; i < TILES; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int p = 4 * (tid + NT * i) + j;
-            const uint32_t kv = order_key(v[4 * i + j]);
-            k[4 * i + j] = p < T ? (p < cl ? kv : kKeyNegInf) : 0u;
-            atomicAdd(&hist[k[4 * i + j] >> 20], 1u);  // the first digit
-        }
 
     // ---- radix select of the threshold key (the topk-th largest): digits of
     //      12, 10 and 10 bits, most significant first.  The wide first digit
@@ -216,9 +211,24 @@ __global__ void __launch_bounds__(NT) indexer_topk_kernel(const float *__restric
         const int bpt = pass == 0 ? bpt0 : bpt1;
         const uint32_t dmask = (uint32_t)nb - 1u;
         uint32_t *h = hist + (pass == 0 ? 0 : kMaxBins + 1024 * (pass - 1));
-        if (pass > 0) {
+        if constexpr (STREAM) {
+            for (int c = 0; c < nchunks; ++c) {
+                next_chunk(c);
 #pragma unroll
-            for (int q = 0; q < 4 * TILES; ++q)
+                for (int q = 0; q < KPT; ++q)
+                    if ((k[q] & pmask) == prefix) atomicAdd(&h[(k[q] >> shift) & dmask], 1u);
+            }
+        } else if (pass == 0) {
+#pragma unroll
+            for (int i = 0; i < TILES; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    key(0, i, j);
+                    atomicAdd(&h[k[4 * i + j] >> 20], 1u);
+                }
+        } else {
+#pragma unroll
+            for (int q = 0; q < KPT; ++q)
                 if ((k[q] & pmask) == prefix) atomicAdd(&h[(k[q] >> shift) & dmask], 1u);
         }
         lds_barrier();
@@ -238,170 +248,78 @@ __global__ void __launch_bounds__(NT) indexer_topk_kernel(const float *__restric
     }
     const uint32_t thr = prefix;  // keys above are all taken, `need` of those equal to it
 
-    // ---- ordered pass: per tile, the keys above the threshold and those equal
-    //      to it, counted two tiles to a word (16-bit fields: a tile holds
-    //      4 NT positions): words [0, TILES / 2) the keys above, the rest the
-    //      equal ones ----
-    uint32_t cnt[TILES] = {};
-#pragma unroll
-    for (int i = 0; i < TILES; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int q = 4 * i + j;
-            const uint32_t f = 1u << (16 * (i & 1));
-            cnt[i >> 1] += k[q] > thr ? f : 0u;
-            cnt[TILES / 2 + (i >> 1)] += k[q] == thr ? f : 0u;
-        }
-    uint32_t excl[TILES];
-#pragma unroll
-    for (int w = 0; w < TILES; ++w) {
-        excl[w] = wave_inclusive_sum(cnt[w]) - cnt[w];
-        if (lane == 63) osum[wave][w] = excl[w] + cnt[w];
-    }
-    lds_barrier();
-    // the wavefronts' totals: lane l < NW takes wavefront l's, a prefix sum over
-    // the lanes gives the counts before this wavefront and the tiles' totals
-    uint32_t before[TILES], total[TILES];
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-#pragma unroll
-    for (int f = 0; f < TILES; ++f) {
-        const uint32_t o = lane < NW ? osum[lane][f] : 0u;
-        const uint32_t incl = row_inclusive_sum(o);
-        before[f] = (uint32_t)__builtin_amdgcn_readlane((int)(incl - o), wave_u);
-        total[f] = (uint32_t)__builtin_amdgcn_readlane((int)incl, NW - 1);
-    }
+    // ---- ordered pass, chunk by chunk: per tile, the keys above the threshold
+    //      and those equal to it, counted two tiles to a word (16-bit fields: a
+    //      tile holds 4 NT positions): words [0, TILES / 2) the keys above, the
+    //      rest the equal ones.  STREAM alternates two sets of wave totals, so a
+    //      chunk's barrier also orders the reads of the totals two chunks back
+    //      before their rewrite. ----
     // compress_lens again, opaque to the compiler: otherwise it keeps the 16 lane
     // masks of the key step alive across the passes for the test below
     int cl_out = cl;
     asm volatile("" : "+s"(cl_out));
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     uint32_t gt_tiles = 0, eq_tiles = 0;  // keys of each kind in the tiles before
+    for (int c = 0; c < nchunks; ++c) {
+        if constexpr (STREAM) next_chunk(c);
+        uint32_t(*os)[TILES] = osum[STREAM ? (c & 1) : 0];
+        uint32_t cnt[TILES] = {};
 #pragma unroll
-    for (int i = 0; i < TILES; ++i) {
-        const int f = i >> 1, sh = 16 * (i & 1);
-        const uint32_t gt_before = gt_tiles + (((before[f] + excl[f]) >> sh) & 0xffffu);
-        const uint32_t eq_before = eq_tiles + (((before[TILES / 2 + f] + excl[TILES / 2 + f]) >> sh) & 0xffffu);
-        // equal keys are taken in position order while their rank among the
-        // equal keys is below need
-        uint32_t pos = gt_before + min(eq_before, need);
-        uint32_t eq_rank = eq_before;
+        for (int i = 0; i < TILES; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int q = 4 * i + j;
-            const int t = 4 * (tid + NT * i) + j;
-            bool take = k[q] > thr;
-            if (k[q] == thr) take = eq_rank++ < need;
-            if (take && pos < (uint32_t)topk) orow[pos++] = t < cl_out ? t + offset : -1;
+            for (int j = 0; j < 4; ++j) {
+                const int q = 4 * i + j;
+                const uint32_t f = 1u << (16 * (i & 1));
+                cnt[i >> 1] += k[q] > thr ? f : 0u;
+                cnt[TILES / 2 + (i >> 1)] += k[q] == thr ? f : 0u;
+            }
+        uint32_t excl[TILES];
+#pragma unroll
+        for (int w = 0; w < TILES; ++w) {
+            excl[w] = wave_inclusive_sum(cnt[w]) - cnt[w];
+            if (lane == 63) os[wave][w] = excl[w] + cnt[w];
         }
-        gt_tiles += (total[f] >> sh) & 0xffffu;
-        eq_tiles += (total[TILES / 2 + f] >> sh) & 0xffffu;
+        lds_barrier();
+        // the wavefronts' totals: lane l < NW takes wavefront l's, a prefix sum
+        // over the lanes gives the counts before this wavefront and the tiles'
+        // totals
+        uint32_t before[TILES], total[TILES];
+#pragma unroll
+        for (int f = 0; f < TILES; ++f) {
+            const uint32_t o = lane < NW ? os[lane][f] : 0u;
+            const uint32_t incl = row_inclusive_sum(o);
+            before[f] = (uint32_t)__builtin_amdgcn_readlane((int)(incl - o), wave_u);
+            total[f] = (uint32_t)__builtin_amdgcn_readlane((int)incl, NW - 1);
+        }
+#pragma unroll
+        for (int i = 0; i < TILES; ++i) {
+            const int f = i >> 1, sh = 16 * (i & 1);
+            const uint32_t gt_before = gt_tiles + (((before[f] + excl[f]) >> sh) & 0xffffu);
+            const uint32_t eq_before =
+                eq_tiles + (((before[TILES / 2 + f] + excl[TILES / 2 + f]) >> sh) & 0xffffu);
+            // equal keys are taken in position order while their rank among the
+            // equal keys is below need
+            uint32_t pos = gt_before + min(eq_before, need);
+            uint32_t eq_rank = eq_before;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int q = 4 * i + j;
+                const int t = c * kKeyCap + 4 * (tid + NT * i) + j;
+                bool take = k[q] > thr;
+                if (k[q] == thr) take = eq_rank++ < need;
+                if (take && pos < (uint32_t)topk) orow[pos++] = t < cl_out ? t + offset : -1;
+            }
+            gt_tiles += (total[f] >> sh) & 0xffffu;
+            eq_tiles += (total[TILES / 2 + f] >> sh) & 0xffffu;
+        }
     }
 }
 
-// Rows longer than kKeyCap: every pass reads the row's scores from memory.
-__global__ void __launch_bounds__(kSelThreads) indexer_topk_stream_kernel(const float *__restrict__ scores, int64_t s,
-                                                                   int32_t T, int64_t start_pos, int32_t ratio,
-                                                                   int32_t topk, int32_t offset,
-                                                                   int32_t *__restrict__ out, int64_t row_stride,
-                                                                   int32_t col0) {
-    __shared__ uint32_t hist[kMaxBins];
-    __shared__ uint32_t sums[kSelThreads / 64];
-    __shared__ uint32_t pick[2];  // digit, count of matching keys above it
-
-    const int tid = threadIdx.x;
-    const int64_t r = blockIdx.x;
-    const int64_t si = r % s;
-    const int64_t cl = start_pos == 0 ? (si + 1) / ratio : (start_pos + s) / ratio;  // compress_lens
-    const float *sr = scores + r * T;
-    int32_t *orow = out + r * row_stride + col0;
-    auto key_of = [&](int t) -> uint32_t { return t < cl ? order_key(sr[t]) : kKeyNegInf; };
-
-    if (topk >= T) {  // every position is taken
-        for (int t = tid; t < T; t += kSelThreads) orow[t] = t < cl ? t + offset : -1;
-        return;
-    }
-    // ---- radix select of the threshold key (the topk-th largest): digits of
-    //      12, 10 and 10 bits, most significant first.  The wide first digit
-    //      (sign, exponent, 3 mantissa bits) spreads scores that share a few
-    //      binades over many bins, so the histogram atomics rarely collide; the
-    //      later digits only count the few keys still matching. ----
-    uint32_t prefix = 0, pmask = 0;
-    uint32_t need = (uint32_t)topk;  // how many keys matching the prefix are still to take
-#pragma unroll 1
-    for (int pass = 0; pass < 3; ++pass) {
-        const int width = pass == 0 ? 12 : 10;
-        const int shift = pass == 0 ? 20 : (pass == 1 ? 10 : 0);
-        const int nb = 1 << width;
-        const uint32_t dmask = (uint32_t)nb - 1u;
-        for (int i = tid; i < nb; i += kSelThreads) hist[i] = 0;
-        __syncthreads();
-#pragma unroll 16
-        for (int t = tid; t < T; t += kSelThreads) {
-            const uint32_t k = key_of(t);
-            if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
-        }
-        __syncthreads();
-        // thread i holds bins [i * bpt, (i + 1) * bpt); the counts above its bins
-        // come from a prefix sum over the threads (total minus the inclusive sum)
-        const int bpt = nb / kSelThreads;
-        uint32_t c = 0;
-        for (int j = 0; j < bpt; ++j) c += hist[tid * bpt + j];
-        uint32_t total;
-        const uint32_t incl = wg_inclusive_sum(c, sums, &total);
-        uint32_t cum = total - incl;  // keys in the bins above this thread's
-        if (cum < need && cum + c >= need) {  // exactly one thread: the threshold bin is here
-            int digit = tid * bpt;
-            for (int j = bpt - 1; j >= 0; --j) {
-                const uint32_t h = hist[tid * bpt + j];
-                if (cum + h >= need) {
-                    digit = tid * bpt + j;
-                    break;
-                }
-                cum += h;
-            }
-            pick[0] = (uint32_t)digit;
-            pick[1] = cum;
-        }
-        __syncthreads();
-        prefix |= pick[0] << shift;
-        pmask |= dmask << shift;
-        need -= pick[1];
-        __syncthreads();  // pick and hist are rewritten by the next pass
-    }
-    const uint32_t thr = prefix;  // keys above are all taken, `need` of those equal to it
-
-    // ---- ordered pass: positions in order, kPerThread consecutive per thread ----
-    uint32_t written = 0, eq_left = need;
-    for (int base = 0; base < T; base += kSelThreads * kPerThread) {
-        const int t0 = base + kPerThread * tid;
-        uint32_t kk[kPerThread];
-        uint32_t n_gt = 0, n_eq = 0;
-#pragma unroll
-        for (int j = 0; j < kPerThread; ++j) {
-            kk[j] = t0 + j < T ? key_of(t0 + j) : 0u;
-            n_gt += (t0 + j < T && kk[j] > thr) ? 1u : 0u;
-            n_eq += (t0 + j < T && kk[j] == thr) ? 1u : 0u;
-        }
-        // (at most kSelThreads * kPerThread = 16384 per tile: two 16-bit counts in one word)
-        uint32_t tot;
-        const uint32_t pre = wg_inclusive_sum(n_gt | (n_eq << 16), sums, &tot) - (n_gt | (n_eq << 16));
-        const uint32_t gt_before = pre & 0xffffu, eq_before = pre >> 16;
-        // equal keys are taken in position order while their rank among the equal
-        // keys still to take is below eq_left
-        uint32_t pos = written + gt_before + min(eq_before, eq_left);
-        uint32_t eq_rank = eq_before;
-#pragma unroll
-        for (int j = 0; j < kPerThread; ++j) {
-            const int t = t0 + j;
-            if (t >= T) break;
-            bool take = kk[j] > thr;
-            if (kk[j] == thr) take = eq_rank++ < eq_left;
-            if (take && pos < (uint32_t)topk) orow[pos++] = t < cl ? t + offset : -1;
-        }
-        const uint32_t tile_eq = tot >> 16;
-        const uint32_t tile_eq_taken = min(tile_eq, eq_left);
-        written += (tot & 0xffffu) + tile_eq_taken;
-        eq_left -= tile_eq_taken;
-    }
+template <bool VEC, bool STREAM>
+void launch_topk(const float *scores, int64_t rows, int64_t s, int32_t n_cols, int64_t start_pos, int32_t ratio,
+                 int32_t topk, int32_t offset, int32_t *idx, int64_t row_stride, int32_t col0, hipStream_t stream) {
+    hipLaunchKernelGGL((indexer_topk_kernel<kSelThreads, VEC, STREAM>), dim3((unsigned)rows), dim3(kSelThreads), 0,
+                       stream, scores, s, n_cols, start_pos, ratio, topk, offset, idx, row_stride, col0);
 }
 
 }  // namespace
@@ -417,18 +335,15 @@ extern "C" sa_status sa_indexer_topk(const float *scores, int64_t b, int64_t s, 
     const int64_t rows = b * s;
     if (rows == 0 || topk == 0) return SA_OK;
     if (!scores || !idx) return SA_ERR_NULL;
-    if (rows > 0x7fffffffLL) return SA_ERR_SHAPE;
-    if (n_cols <= kKeyCap && (n_cols & 3) == 0 && ((uintptr_t)scores & 15) == 0)
-        hipLaunchKernelGGL((indexer_topk_kernel<kSelThreads, true>), dim3((unsigned)rows), dim3(kSelThreads), 0,
-                           (hipStream_t)stream, scores, s, n_cols, start_pos, ratio, topk, offset, idx, row_stride,
-                           col0);
-    else if (n_cols <= kKeyCap)
-        hipLaunchKernelGGL((indexer_topk_kernel<kSelThreads, false>), dim3((unsigned)rows), dim3(kSelThreads), 0,
-                           (hipStream_t)stream, scores, s, n_cols, start_pos, ratio, topk, offset, idx, row_stride,
-                           col0);
-    else
-        hipLaunchKernelGGL(indexer_topk_stream_kernel, dim3((unsigned)rows), dim3(kSelThreads), 0,
-                           (hipStream_t)stream, scores, s, n_cols, start_pos, ratio, topk, offset, idx, row_stride,
-                           col0);
+    if (rows > 0x7fffffffLL || n_cols > 0x7fff0000) return SA_ERR_SHAPE;  // chunk positions stay in int
+    const bool vec = (n_cols & 3) == 0 && ((uintptr_t)scores & 15) == 0;
+    const hipStream_t st = (hipStream_t)stream;
+    if (n_cols <= kKeyCap) {
+        if (vec) launch_topk<true, false>(scores, rows, s, n_cols, start_pos, ratio, topk, offset, idx, row_stride, col0, st);
+        else launch_topk<false, false>(scores, rows, s, n_cols, start_pos, ratio, topk, offset, idx, row_stride, col0, st);
+    } else {
+        if (vec) launch_topk<true, true>(scores, rows, s, n_cols, start_pos, ratio, topk, offset, idx, row_stride, col0, st);
+        else launch_topk<false, true>(scores, rows, s, n_cols, start_pos, ratio, topk, offset, idx, row_stride, col0, st);
+    }
     return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
