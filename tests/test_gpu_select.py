@@ -1,6 +1,6 @@
 """GPU parity of the indexer's selection tail (sa_indexer_topk): bit for bit
 against the oracle (both take equal scores at the lower position first), on
-decode rows short enough for LDS and longer ones, causal prefill masks, the
+decode rows held in registers and longer ones read in chunks, causal prefill masks, the
 take-everything case, heavy ties, -inf scores, zeros of both signs straddling
 the k-th score (equal scores: -0.0 and +0.0 rank alike), and writes into the
 compressed columns of a wider index buffer (other columns untouched)."""
@@ -40,6 +40,8 @@ CASES = [
     (13, 6, 1, 40000, 3, 1500, 128, "normal"),     # decode: 13333 positions (odd: element loads, all tiles)
     (14, 4, 1, 65536, 4, 2048, 128, "normal"),     # decode: T = 16384, the register form's cap
     (15, 3, 1, 65539, 4, 3000, 128, "normal"),     # decode: T = 16385, one past the cap (streaming form)
+    (17, 2, 1, 100000, 3, 2048, 128, "normal"),    # decode: T = 33333, streaming with element loads
+    (18, 2, 1, 524287, 4, 4096, 128, "ties"),      # decode: T = 131072, equal keys taken across 8 chunks
 ]
 
 
