@@ -14,6 +14,8 @@
 // each kept position its output column -- so the output comes out in position
 // order with no sort.  Rows of up to kKeyCap positions keep their keys in
 // registers; longer rows are read again, chunk by chunk, in each pass.
+#include <type_traits>
+
 #include "sa_device.h"
 #include "../../include/sparse_attn.h"
 
@@ -63,8 +65,8 @@ __device__ __forceinline__ uint32_t row_inclusive_sum(uint32_t x) {
 }
 
 // The digit of the need-th largest key among those a histogram counted (BPT
-// consecutive bins per thread, bins in thread order) and the number of keys in
-// the bins above that digit.  wsum[w] holds the count of wavefront w's bins.
+// consecutive bins per thread, bins in thread order), the number of keys in
+// the bins above that digit and the number in its own bin.  wsum[w] holds the count of wavefront w's bins.
 // Every wavefront finds the digit by itself, with no barrier and no loop over
 // the wavefronts: lane l < NW takes wavefront NW - 1 - l's total, so the lanes'
 // prefix sum counts from the highest bins down and a ballot names the
@@ -72,7 +74,7 @@ __device__ __forceinline__ uint32_t row_inclusive_sum(uint32_t x) {
 // the histogram, name the lane and then the bin.
 template <int NT, int BPT>
 __device__ __forceinline__ void find_digit(const uint32_t *hist, const uint32_t *wsum, uint32_t need,
-                                           uint32_t &digit, uint32_t &above) {
+                                           uint32_t &digit, uint32_t &above, uint32_t &count) {
     constexpr int NW = NT / 64;
     static_assert(NW <= 16, "the wave totals are scanned within one row of 16 lanes");
     const int lane = threadIdx.x & 63;
@@ -98,12 +100,13 @@ __device__ __forceinline__ void find_digit(const uint32_t *hist, const uint32_t 
     const uint32_t incl = wave_inclusive_sum(c);
     uint32_t cum = above_w + (tot_ws - incl);  // keys in the bins above this lane's
     const bool hit = cum < need && cum + c >= need;
-    uint32_t d = (uint32_t)(th * BPT);
+    uint32_t d = (uint32_t)(th * BPT), dc = 0;
     bool done = false;
 #pragma unroll
     for (int j = BPT - 1; j >= 0; --j) {
         const bool here = !done && cum + bins[j] >= need;
         d = here ? (uint32_t)(th * BPT + j) : d;
+        dc = here ? bins[j] : dc;
         cum += (!done && !here) ? bins[j] : 0u;
         done = done || here;
     }
@@ -111,6 +114,7 @@ __device__ __forceinline__ void find_digit(const uint32_t *hist, const uint32_t 
     const int src = m ? __builtin_ctzll(m) : 0;
     digit = (uint32_t)__builtin_amdgcn_readlane((int)d, src);
     above = (uint32_t)__builtin_amdgcn_readlane((int)cum, src);
+    count = (uint32_t)__builtin_amdgcn_readlane((int)dc, src);
 }
 
 // One row per workgroup of NT threads, taken in chunks of kKeyCap positions:
@@ -202,6 +206,7 @@ __global__ void __launch_bounds__(NT) indexer_topk_kernel(const float *__restric
     //      later digits only count the few keys still matching. ----
     uint32_t prefix = 0, pmask = 0;
     uint32_t need = (uint32_t)topk;  // how many keys matching the prefix are still to take
+    uint32_t n_eq = 0;               // keys in the last digit's bin: those equal to the threshold
 #pragma unroll
     for (int pass = 0; pass < 3; ++pass) {
         const int width = pass == 0 ? 12 : 10;
@@ -239,43 +244,52 @@ __global__ void __launch_bounds__(NT) indexer_topk_kernel(const float *__restric
         lds_barrier();
         uint32_t digit, above;
         if (pass == 0)
-            find_digit<NT, bpt0>(h, wsum[pass], need, digit, above);
+            find_digit<NT, bpt0>(h, wsum[pass], need, digit, above, n_eq);
         else
-            find_digit<NT, bpt1>(h, wsum[pass], need, digit, above);
+            find_digit<NT, bpt1>(h, wsum[pass], need, digit, above, n_eq);
         prefix |= digit << shift;
         pmask |= dmask << shift;
         need -= above;
     }
     const uint32_t thr = prefix;  // keys above are all taken, `need` of those equal to it
 
-    // ---- ordered pass, chunk by chunk: per tile, the keys above the threshold
-    //      and those equal to it, counted two tiles to a word (16-bit fields: a
-    //      tile holds 4 NT positions): words [0, TILES / 2) the keys above, the
-    //      rest the equal ones.  STREAM alternates two sets of wave totals, so a
-    //      chunk's barrier also orders the reads of the totals two chunks back
-    //      before their rewrite. ----
+    // ---- ordered pass, chunk by chunk: per tile, the keys taken counted two
+    //      tiles to a word (16-bit fields: a tile holds 4 NT positions).  When
+    //      every key equal to the threshold is taken (n_eq == need: the usual
+    //      case, no tie at the cut) that is one count, of the keys at or above
+    //      it; otherwise words [0, TILES / 2) count the keys above and the rest
+    //      the equal ones, which are taken in position order while their rank
+    //      among the equal keys is below need.  STREAM alternates two sets of
+    //      wave totals, so a chunk's barrier also orders the reads of the totals
+    //      two chunks back before their rewrite. ----
     // compress_lens again, opaque to the compiler: otherwise it keeps the 16 lane
     // masks of the key step alive across the passes for the test below
     int cl_out = cl;
     asm volatile("" : "+s"(cl_out));
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     uint32_t gt_tiles = 0, eq_tiles = 0;  // keys of each kind in the tiles before
-    for (int c = 0; c < nchunks; ++c) {
+    auto ordered_chunk = [&](int c, auto all_tag) {
+        constexpr bool ALL = decltype(all_tag)::value;
+        constexpr int NC = ALL ? TILES / 2 : TILES;  // count words
         if constexpr (STREAM) next_chunk(c);
         uint32_t(*os)[TILES] = osum[STREAM ? (c & 1) : 0];
-        uint32_t cnt[TILES] = {};
+        uint32_t cnt[NC] = {};
 #pragma unroll
         for (int i = 0; i < TILES; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int q = 4 * i + j;
                 const uint32_t f = 1u << (16 * (i & 1));
-                cnt[i >> 1] += k[q] > thr ? f : 0u;
-                cnt[TILES / 2 + (i >> 1)] += k[q] == thr ? f : 0u;
+                if constexpr (ALL) {
+                    cnt[i >> 1] += k[q] >= thr ? f : 0u;
+                } else {
+                    cnt[i >> 1] += k[q] > thr ? f : 0u;
+                    cnt[TILES / 2 + (i >> 1)] += k[q] == thr ? f : 0u;
+                }
             }
-        uint32_t excl[TILES];
+        uint32_t excl[NC];
 #pragma unroll
-        for (int w = 0; w < TILES; ++w) {
+        for (int w = 0; w < NC; ++w) {
             excl[w] = wave_inclusive_sum(cnt[w]) - cnt[w];
             if (lane == 63) os[wave][w] = excl[w] + cnt[w];
         }
@@ -283,9 +297,9 @@ __global__ void __launch_bounds__(NT) indexer_topk_kernel(const float *__restric
         // the wavefronts' totals: lane l < NW takes wavefront l's, a prefix sum
         // over the lanes gives the counts before this wavefront and the tiles'
         // totals
-        uint32_t before[TILES], total[TILES];
+        uint32_t before[NC], total[NC];
 #pragma unroll
-        for (int f = 0; f < TILES; ++f) {
+        for (int f = 0; f < NC; ++f) {
             const uint32_t o = lane < NW ? os[lane][f] : 0u;
             const uint32_t incl = row_inclusive_sum(o);
             before[f] = (uint32_t)__builtin_amdgcn_readlane((int)(incl - o), wave_u);
@@ -294,24 +308,40 @@ __global__ void __launch_bounds__(NT) indexer_topk_kernel(const float *__restric
 #pragma unroll
         for (int i = 0; i < TILES; ++i) {
             const int f = i >> 1, sh = 16 * (i & 1);
+            const int t0 = c * kKeyCap + 4 * (tid + NT * i);
             const uint32_t gt_before = gt_tiles + (((before[f] + excl[f]) >> sh) & 0xffffu);
-            const uint32_t eq_before =
-                eq_tiles + (((before[TILES / 2 + f] + excl[TILES / 2 + f]) >> sh) & 0xffffu);
-            // equal keys are taken in position order while their rank among the
-            // equal keys is below need
-            uint32_t pos = gt_before + min(eq_before, need);
-            uint32_t eq_rank = eq_before;
+            if constexpr (ALL) {
+                uint32_t pos = gt_before;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int q = 4 * i + j;
-                const int t = c * kKeyCap + 4 * (tid + NT * i) + j;
-                bool take = k[q] > thr;
-                if (k[q] == thr) take = eq_rank++ < need;
-                if (take && pos < (uint32_t)topk) orow[pos++] = t < cl_out ? t + offset : -1;
+                for (int j = 0; j < 4; ++j) {
+                    const bool take = k[4 * i + j] >= thr;
+                    if (take && pos < (uint32_t)topk) orow[pos] = t0 + j < cl_out ? t0 + j + offset : -1;
+                    pos += take ? 1u : 0u;
+                }
+            } else {
+                const uint32_t eq_before =
+                    eq_tiles + (((before[TILES / 2 + f] + excl[TILES / 2 + f]) >> sh) & 0xffffu);
+                uint32_t pos = gt_before + min(eq_before, need);
+                uint32_t eq_rank = eq_before;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int q = 4 * i + j;
+                    bool take = k[q] > thr;
+                    if (k[q] == thr) take = eq_rank++ < need;
+                    if (take && pos < (uint32_t)topk) orow[pos] = t0 + j < cl_out ? t0 + j + offset : -1;
+                    pos += take ? 1u : 0u;
+                }
+                eq_tiles += (total[TILES / 2 + f] >> sh) & 0xffffu;
             }
             gt_tiles += (total[f] >> sh) & 0xffffu;
-            eq_tiles += (total[TILES / 2 + f] >> sh) & 0xffffu;
         }
+    };
+    const bool all_eq = n_eq == need;
+    for (int c = 0; c < nchunks; ++c) {
+        if (all_eq)
+            ordered_chunk(c, std::true_type{});
+        else
+            ordered_chunk(c, std::false_type{});
     }
 }
 
