@@ -91,6 +91,21 @@ __device__ __forceinline__ void dma_4B(const void *src, uint32_t lds_base) {
                  : "memory", "m0");
 }
 
+// Partial waits.  s_waitcnt vmcnt(N) returns once at most N of this wave's
+// vector-memory operations are outstanding.  A wave's loads, these copies
+// included, complete in the order it issued them, so while a copy is
+// outstanding every load issued after it is too: if the wave issued at least N
+// loads or copies after the ones it needs, vmcnt(N) returns only when those
+// are done.  Stores do not count toward N: one may complete ahead of earlier
+// loads, but while the needed copy is outstanding the N loads behind it keep
+// the count above N; extra loads in between (the compiler's own) only make the
+// wait longer.  Every partial wait in the kernels names the copies issued
+// behind the ones it waits for; each is one instruction of the whole wave,
+// issued with at least one lane active (an instruction with none may be
+// skipped by an exec branch and then does not count).  The compiler's waits for
+// its own loads count only its own operations, so a copy issued after one of
+// its loads only lengthens them.
+//
 // Wait until at most N vector-memory operations of this wave are outstanding,
 // then barrier the workgroup (all LDS writes of completed copies visible).
 template <int N>
