@@ -7,6 +7,9 @@ lists built, compressed positions appended (when the workload has them) and
 the sparse attention itself -- all through the C ABI on one stream.  Decode
 workloads run the step as one launch (sa_sparse_attn_decode_step, the lists
 built inside the attention kernel); ``--unfused`` times the separate calls.
+Prefill workloads run the separate calls; ``--prefill-list-in-kernel`` runs
+them as two launches instead (the chunk's fp8 round trip, then
+sa_sparse_attn_prefill_step with the lists built inside the attention kernel).
 ``--kv8`` holds the decode cache fp8-resident (e4m3fn codes + E8M0 block
 scales) and runs the one-launch step on it: the same results, bit for bit,
 from about half the gathered bytes.  ``--rope`` fuses the output's inverse
@@ -73,6 +76,9 @@ def parse():
     ap.add_argument("--unfused", action="store_true",
                     help="decode: run the step as separate calls (ring update, lists, attention) "
                          "instead of the one-launch decode step")
+    ap.add_argument("--prefill-list-in-kernel", action="store_true",
+                    help="prefill: build the index lists inside the attention kernel "
+                         "(sa_sparse_attn_prefill_step) instead of the separate list calls")
     ap.add_argument("--kv8", action="store_true",
                     help="decode: the cache held fp8-resident (e4m3fn codes + E8M0 block scales) and read "
                          "and written in that form by the one-launch step (bitwise the same results)")
@@ -92,7 +98,8 @@ def algorithmic_work(w, idx_sets, fused=False, kv8=False):
     """Algorithmic bytes and flops of one attention launch (valid entries only).
     Decode: every valid gathered row is HBM traffic (rows differ per sequence).
     Prefill: the unique KV rows referenced are read once; repeats come from cache.
-    Fused decode step: the list is written instead of read (compressed entries
+    Fused prefill: the list is built in the kernel, only the compressed entries
+    are read.  Fused decode step: the list is written instead of read (compressed entries
     still read), and the new row is read once and written once into the ring
     (it enters the attention from registers instead of the ring).  kv8: a row is
     d code bytes plus its 16-byte scale record; the new row is read as bf16 and
@@ -114,7 +121,9 @@ def algorithmic_work(w, idx_sets, fused=False, kv8=False):
             u = idx[bi].flatten()
             uniq += int(torch.unique(u[u >= 0]).numel())
         kv_bytes = uniq * w.d * 2
-    if fused:
+    if fused and w.start_pos == 0:
+        idx_bytes = w.b * w.s * w.n_comp * 4   # the compressed positions; the list stays in the kernel
+    elif fused:
         idx_bytes += w.b * w.s * w.n_comp * 4
         kv_bytes += w.b * w.d * 2     # new row: read raw + written, minus the gathered copy the count holds
     total = q_bytes + o_bytes + idx_bytes + sink_bytes + kv_bytes
@@ -424,12 +433,21 @@ def main():
     sets = [pipeline.prepare(args.workload, raw0, kv8=args.kv8, rope_dim=rope_dim)]
     pipeline.build_index(sets[0])
     torch.cuda.synchronize()
-    fused = w.start_pos > 0 and not args.unfused
+    # decode: the one-launch step unless --unfused; prefill: the separate calls
+    # unless --prefill-list-in-kernel (without the output rotation)
+    if args.prefill_list_in_kernel and (w.start_pos > 0 or rope_dim or args.unfused):
+        print("bench.py: --prefill-list-in-kernel applies to the prefill workloads (3, 5), without --rope",
+              file=sys.stderr)
+        sys.exit(2)
+    fused = (w.start_pos > 0 and not args.unfused) or args.prefill_list_in_kernel
     if args.kv8:
         step_fn = kern_fn = pipeline.step_fused_kv8
-    else:
+    elif w.start_pos > 0:
         step_fn = pipeline.step_fused if fused else pipeline.step
         kern_fn = pipeline.step_fused if fused else pipeline.attend    # the dominant kernel's launch
+    else:
+        step_fn = pipeline.step_fused_prefill if fused else pipeline.step
+        kern_fn = pipeline.attend_fused_prefill if fused else pipeline.attend
     work = algorithmic_work(w, [sets[0].idx], fused, args.kv8)
     if rope_dim:
         work["bytes"] += w.b * w.s * rope_dim * 4       # each query's table row
@@ -522,7 +540,8 @@ def main():
         achieved = work["flops"] / (attn_mean / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
-    roof["traffic"] = measured_traffic(traffic_tag(args.workload, fused or w.start_pos == 0, args.kv8, rope_dim))
+    tag = traffic_tag(args.workload, fused or w.start_pos == 0, args.kv8, rope_dim)
+    roof["traffic"] = measured_traffic(tag + ("_inlist" if args.prefill_list_in_kernel else ""))
     roof["algorithmic_bytes"] = work["bytes"]
     roof["algorithmic_flops"] = work["flops"]
     roof["kernel_ms_mean"] = round(attn_mean, 5)
@@ -544,7 +563,8 @@ def main():
         "config": {"workload": w.name, "batch": w.b, "queries_per_seq": w.s, "heads": w.h, "head_dim": w.d,
                    "topk": w.topk, "kv_rows_per_seq": w.rows, "valid_entries": work["valid"],
                    "input_sets": n_sets, "launch": launch_desc,
-                   "step": "one-launch decode step" if fused else "separate calls",
+                   "step": ("separate calls" if not fused else "one-launch decode step" if w.start_pos > 0
+                            else "chunk fp8 round trip, then attention with the list built in the kernel"),
                    "kv_cache": "fp8 e4m3fn codes + E8M0 block scales" if args.kv8 else "bf16",
                    "output_rotation": f"inverse rotary embedding of the last {rope_dim} values, fused"
                    if rope_dim else "none",

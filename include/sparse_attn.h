@@ -311,6 +311,49 @@ sa_status sa_sparse_attn_decode_step(const uint16_t *q, uint16_t *kv, const uint
                                      int32_t kernel, int32_t splits);
 
 /* ------------------------------------------------------------------------
+ * Prefill with the list built in the attention kernel -- [QLAT]
+ * Attention.forward at position 0 (the window list of the chunk, the
+ * compressed indices concatenated after it, sparse_attn), [ATTEND]
+ * get_window_topk_idxs (prefill branch).
+ *
+ * Same result as these calls, with wcols = min(s, window):
+ *   sa_window_topk_idxs(window, b, s, 0, idx, wcols + kc)
+ *   sa_append_compressed_idxs(idx, wcols + kc, wcols, cidx, b * s, kc, s)
+ *   sa_sparse_attn(q, kv, sink, idx, b, s, h, d, rows, wcols + kc, scale, out)
+ * without the list's trip through memory: each workgroup of the pair kernel
+ * builds its query's list in LDS (query t takes chunk rows max(0, t - window +
+ * 1) + j while <= t, then cidx entries + s).  The chunk's rows must already hold their fp8 round
+ * trip (sa_window_kv_update on the chunk, or sa_act_quant_fp8_inplace).
+ *
+ *   q       [b][s][h][d]     bf16  the chunk's queries, positions 0 .. s-1
+ *   kv      [b][rows][d]     bf16  per sequence: rows [0, s) the chunk, rows
+ *                                  [s, rows) the compressed cache
+ *   sink    [h]              f32
+ *   cidx    [b][s][kc]       int32 compressed positions (-1 = none); may be NULL
+ *                                  when kc == 0; entry c addresses kv row s + c
+ *   idx_out [b][s][wcols+kc] int32 NULL, or receives the concatenated list (what
+ *                                  the calls above would leave in idx)
+ *   out     [b][s][h][d]     bf16
+ * window >= 1; rows >= s; d in {64, 128, 256, 512}; kc >= 0.  Pointers of
+ * bf16 data 16-byte aligned (else SA_ERR_SHAPE).  Tolerance, determinism and
+ * the index rules are those of sa_sparse_attn; entries outside [0, rows) are
+ * skipped like -1.
+ *
+ * kernel: 0 or SA_KERNEL_PAIR (the pair kernel builds this list; any other
+ * value: SA_ERR_UNSUPPORTED); splits: as for sa_sparse_attn_ex (0 = automatic).
+ * workspace: at least sa_sparse_attn_prefill_step_workspace_bytes(b, s, h, d,
+ * window, kc, kernel, splits) bytes, 16-byte aligned (may be NULL when that is
+ * 0). */
+size_t sa_sparse_attn_prefill_step_workspace_bytes(int64_t b, int64_t s, int32_t h, int32_t d, int32_t window,
+                                                   int32_t kc, int32_t kernel, int32_t splits);
+
+sa_status sa_sparse_attn_prefill_step(const uint16_t *q, const uint16_t *kv, const float *sink,
+                                      const int32_t *cidx, int32_t *idx_out, int64_t b, int64_t s, int32_t h,
+                                      int32_t d, int64_t rows, int32_t window, int32_t kc, float scale,
+                                      uint16_t *out, void *workspace, size_t workspace_bytes, void *stream,
+                                      int32_t kernel, int32_t splits);
+
+/* ------------------------------------------------------------------------
  * Sparse latent attention over fp8-resident rows -- the operation of
  * sa_sparse_attn and sa_sparse_attn_decode_step with the latent rows held as
  * kv8 codes + scale records (layout as for sa_kv8_pack) instead of bf16:

@@ -86,11 +86,16 @@ def lib() -> ctypes.CDLL:
         L.sa_sparse_attn_noalloc_scratch_bytes.argtypes = []
         L.sa_sparse_attn_noalloc_scratch_bytes.restype = sz
         L.sa_sparse_attn_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i64, i32, f32, vp, vp, i32, i32]
+        L.sa_sparse_attn_prefill_step_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32, i32, i32]
+        L.sa_sparse_attn_prefill_step_workspace_bytes.restype = sz
+        L.sa_sparse_attn_prefill_step.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i64, i32, i32, f32, vp,
+                                                  vp, sz, vp, i32, i32]
         for fn in ("sa_window_topk_idxs_shape", "sa_window_topk_idxs", "sa_append_compressed_idxs",
                    "sa_act_quant_fp8_inplace", "sa_window_kv_update", "sa_sparse_attn", "sa_sparse_attn_ex",
                    "sa_sparse_attn_decode_step", "sa_kv8_pack", "sa_kv8_unpack", "sa_sparse_attn_kv8",
                    "sa_sparse_attn_decode_step_kv8", "sa_apply_rotary", "sa_sparse_attn_rope",
-                   "sa_sparse_attn_decode_step_rope", "sa_indexer_topk", "sa_sparse_attn_noalloc"):
+                   "sa_sparse_attn_decode_step_rope", "sa_indexer_topk", "sa_sparse_attn_noalloc",
+                   "sa_sparse_attn_prefill_step"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -317,6 +322,59 @@ def sparse_attn_decode_step(q: torch.Tensor, kv: torch.Tensor, kv_new: torch.Ten
                lib().sa_sparse_attn_decode_step_rope(*args, table.data_ptr(), table.shape[0], rope_dim))
         return out
     _check("sa_sparse_attn_decode_step", lib().sa_sparse_attn_decode_step(*args))
+    return out
+
+
+def prefill_step_workspace_bytes(b: int, s: int, h: int, d: int, window: int, kc: int,
+                                 variant: tuple | None = None) -> int:
+    k, sp = variant if variant is not None else (0, 0)
+    return int(lib().sa_sparse_attn_prefill_step_workspace_bytes(b, s, h, d, window, kc, k, sp))
+
+
+def sparse_attn_prefill_step(q: torch.Tensor, kv: torch.Tensor, sink: torch.Tensor, window: int, scale: float,
+                             cidx: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                             idx_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                             variant: tuple | None = None, stream=None) -> torch.Tensor:
+    """Prefill attention with the index list built in the kernel: q [b][s][h][d] at
+    positions 0 .. s-1, kv [b][rows][d] (rows [0, s) the chunk, already through its
+    fp8 round trip; compressed rows after), the window list (min(s, window)
+    columns) + cidx [b][s][kc] (+s) as the index list, built by the pair kernel
+    (``variant`` may only name it).  ``idx_out`` ([b][s][min(s, window) + kc]
+    int32) receives the list when given."""
+    _dev(q, "q", torch.bfloat16)
+    _dev(kv, "kv", torch.bfloat16)
+    _dev(sink, "sink", torch.float32)
+    b, rows, d = kv.shape
+    if q.dim() != 4 or q.shape[0] != b or q.shape[-1] != d:
+        raise ValueError(f"q must be [{b}][s][h][{d}], got {tuple(q.shape)}")
+    s, h = q.shape[1], q.shape[2]
+    if sink.shape != (h,):
+        raise ValueError(f"sink must be [{h}]")
+    kc = 0
+    if cidx is not None:
+        _dev(cidx, "cidx", torch.int32)
+        kc = cidx.shape[-1]
+        if cidx.numel() != b * s * kc:
+            raise ValueError(f"cidx must be [{b}][{s}][kc], got {tuple(cidx.shape)}")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", torch.bfloat16)
+    if idx_out is not None:
+        _dev(idx_out, "idx_out", torch.int32)
+        if idx_out.numel() != b * s * (min(s, window) + kc):
+            raise ValueError(f"idx_out must hold [{b}][{s}][{min(s, window) + kc}]")
+    k, sp = variant if variant is not None else (0, 0)
+    need = prefill_step_workspace_bytes(b, s, h, d, window, kc, variant)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("sa_sparse_attn_prefill_step",
+           lib().sa_sparse_attn_prefill_step(q.data_ptr(), kv.data_ptr(), sink.data_ptr(),
+                                             cidx.data_ptr() if cidx is not None else None,
+                                             idx_out.data_ptr() if idx_out is not None else None, b, s, h, d, rows,
+                                             window, kc, float(scale), out.data_ptr(), ws_ptr, ws_bytes,
+                                             _stream(stream), k, sp))
     return out
 
 

@@ -90,8 +90,9 @@ struct AttnParams {
     uint16_t *kv_ring;       // == kv, writable: ring slot new_slot receives the rounded row
     const int32_t *cidx;     // [nq][kc] compressed positions (-1 = none)
     int32_t *idx_out;        // [nq][topk] concatenated list written out, or null
-    int64_t pos;             // position of the step's token (start_pos >= 1)
-    int32_t window;          // ring slots = window-list columns
+    int64_t pos;             // position of the step's token (start_pos >= 1); -1 for the
+                             // pair kernel's prefill list
+    int32_t window;          // ring slots = window-list columns (prefill list: min(s, window))
     int32_t kc;              // compressed columns
     int32_t wbase;           // (pos + 1) % window: slot of the oldest entry
     int32_t new_slot;        // pos % window: slot of the new row (list entry window - 1)
@@ -112,19 +113,51 @@ struct AttnParams {
     uint8_t *kv8s_ring;
 };
 
-// Entry e of a decode step's concatenated list: the ring listed oldest first,
-// -1 for slots not yet written ("DeepSeek V4.1 ... attention / attend",
-// get_window_topk_idxs, decode branch), then the compressed positions shifted
-// past the ring rows, -1 kept ("... / query-latent", Attention.forward and the
-// Indexer tail).
-__device__ __forceinline__ int step_entry(const AttnParams &p, uint32_t qi, int e) {
-    if (e < p.window) {
-        int slot = p.wbase + e;
-        if (slot >= p.window) slot -= p.window;
-        return (int64_t)slot <= p.pos ? slot : -1;
+// The window part of a list built in the kernel, for one query, in one form
+// for both cases: entry e is row (first + e), less wrap once it reaches wrap,
+// valid while <= last; compressed position c becomes entry c + coff.
+//  * decode step: the ring listed oldest first (first = (pos + 1) % W, wrap =
+//    W), -1 for slots past pos (not yet written); compressed rows follow the
+//    ring's W rows;
+//  * prefill (PREFILL, the pair kernel's own instance): the query at chunk
+//    position t takes chunk rows max(0, t - W + 1) + e, -1 past t (window =
+//    min(s, W) columns; for s < W the first row is 0 either way); compressed
+//    rows follow the chunk's s rows.
+// ("DeepSeek V4.1 ... attention / attend", get_window_topk_idxs; "... /
+// query-latent", Attention.forward and the Indexer tail.)
+struct ListForm {
+    int first, wrap, coff;
+    int64_t last;
+};
+template <bool PREFILL>
+__device__ __forceinline__ ListForm list_form(const AttnParams &p, uint32_t qi) {
+    ListForm f;
+    if constexpr (PREFILL) {
+        const int t = (int)(qi % (uint32_t)p.s);
+        f.first = max(0, t - p.window + 1);
+        f.wrap = 0x7fffffff;
+        f.last = t;
+        f.coff = p.s;
+    } else {
+        f.first = p.wbase;
+        f.wrap = p.window;
+        f.last = p.pos;
+        f.coff = p.window;
     }
-    const int c = p.cidx[(int64_t)qi * p.kc + (e - p.window)];
-    return c < 0 ? -1 : (int)((uint32_t)c + (uint32_t)p.window);
+    return f;
+}
+__device__ __forceinline__ int window_entry(const ListForm &f, int e) {
+    int r = f.first + e;
+    if (r >= f.wrap) r -= f.wrap;
+    return (int64_t)r <= f.last ? r : -1;
+}
+__device__ __forceinline__ int compressed_entry(const ListForm &f, int c) {
+    return c < 0 ? -1 : (int)((uint32_t)c + (uint32_t)f.coff);
+}
+// Entry e of the concatenated list: the window entries, then the compressed ones.
+__device__ __forceinline__ int step_entry(const AttnParams &p, const ListForm &f, uint32_t qi, int e) {
+    if (e < p.window) return window_entry(f, e);
+    return compressed_entry(f, p.cidx[(int64_t)qi * p.kc + (e - p.window)]);
 }
 
 __device__ __forceinline__ bf16x8_t lds_read_b128(const SA_LDS char *p) {
@@ -341,6 +374,17 @@ struct Compactor {
         for (int k = 0; k < K; ++k) {
             const int e = c0 + k * NT + (int)threadIdx.x;
             v[k] = e < c1 ? list[e - c0] : -1;
+        }
+    }
+
+    // prefill list: the window entries by formula, the compressed ones from
+    // list[] (raw positions copied there directly, entry e at list[e - c0])
+    __device__ __forceinline__ void load_lds_prefill(const int *list, int c0, int c1, const ListForm &f,
+                                                     int window) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int e = c0 + k * NT + (int)threadIdx.x;
+            v[k] = e >= c1 ? -1 : (e < window ? window_entry(f, e) : compressed_entry(f, list[e - c0]));
         }
     }
 
@@ -570,8 +614,9 @@ __global__ void __launch_bounds__(WideCfg<D>::THREADS, 1) sa_attn_wide(const Att
     const int lo = (int)sp * p.split_len;
     const int hi = min(p.topk, lo + p.split_len);
     const int32_t *idxq = FUSED ? nullptr : p.idx + (int64_t)qi * p.topk;
-    auto fetch = [&](int e) -> int { return FUSED ? step_entry(p, qi, e) : idxq[e]; };
-    // fused step: the new row's entry (window - 1) in this workgroup's range
+    const ListForm lform = list_form<false>(p, qi);
+    auto fetch = [&](int e) -> int { return FUSED ? step_entry(p, lform, qi, e) : idxq[e]; };
+    // fused decode step: the new row's entry (window - 1) in this workgroup's range
     const bool has_new = FUSED && p.window - 1 >= lo && p.window - 1 < hi;
     u32x4_t new_raw = {0u, 0u, 0u, 0u};
     if (has_new && wave == 0 && chunk_lane)
@@ -900,9 +945,11 @@ struct PairCfg {
     static_assert(KS >= 4 && DT >= 2 && RPW == 16, "tiling");
 };
 
-template <int D, int LCAP, bool FUSED, bool SPLIT>
+template <int D, int LCAP, int MODE, bool SPLIT>
 __global__ void __launch_bounds__(128, 2) sa_attn_pair(const AttnParams p) {
     using C = PairCfg<D, LCAP>;
+    constexpr bool FUSED = MODE == 1;    // decode step: the list built in registers, the new row
+    constexpr bool PREFILL = MODE == 2;  // prefill list: compressed positions copied, window by formula
     static_assert(C::THREADS == 128, "launch bounds");
     // Two workgroups share a CU.  Started together on lists of one length, they
     // would keep entering their HBM-bound phases (index list and Q in, output
@@ -935,7 +982,9 @@ __global__ void __launch_bounds__(128, 2) sa_attn_pair(const AttnParams p) {
 
     const int lo = (int)sp * p.split_len;
     const int hi = min(p.topk, lo + p.split_len);
-    const int32_t *idxq = FUSED ? nullptr : p.idx + (int64_t)qi * p.topk;
+    const int32_t *idxq = MODE == 0 ? p.idx + (int64_t)qi * p.topk : nullptr;
+    const int32_t *cq = PREFILL ? p.cidx + (int64_t)qi * p.kc - p.window : nullptr;  // entry e >= window: cq[e]
+    const ListForm lform = list_form<PREFILL>(p, qi);
     const bool has_new = FUSED && p.window - 1 >= lo && p.window - 1 < hi;
     u32x4_t new_raw = {0u, 0u, 0u, 0u};
     if (has_new && wave == 0 && chunk_lane)
@@ -945,13 +994,21 @@ __global__ void __launch_bounds__(128, 2) sa_attn_pair(const AttnParams p) {
     // directly (4 bytes a lane, 64 entries a wave instruction, entry e at
     // list[e - c0]): Q's copies then go out right behind them, and the wait for
     // the entries (vmcnt counts completions in issue order) leaves Q in flight --
-    // the two memory round trips overlap instead of following each other.
+    // the two memory round trips overlap instead of following each other.  The
+    // prefill list copies only its compressed positions that way; its window
+    // entries are formed when the entries are read back.
     Compactor<C::THREADS, C::LIST_CAP> cmp;
     const uint32_t list_base = lds_addr((const SA_LDS void *)list);
     auto copy_idx = [&](int c0, int c1) {
+        if constexpr (PREFILL) {
 #pragma unroll 1
-        for (int e0 = c0 + wave * 64; e0 < c1; e0 += C::THREADS)
-            if (e0 + lane < c1) dma_4B(idxq + e0 + lane, list_base + (uint32_t)(e0 - c0) * 4);
+            for (int e0 = max(c0, p.window) + wave * 64; e0 < c1; e0 += C::THREADS)
+                if (e0 + lane < c1) dma_4B(cq + e0 + lane, list_base + (uint32_t)(e0 - c0) * 4);
+        } else {
+#pragma unroll 1
+            for (int e0 = c0 + wave * 64; e0 < c1; e0 += C::THREADS)
+                if (e0 + lane < c1) dma_4B(idxq + e0 + lane, list_base + (uint32_t)(e0 - c0) * 4);
+        }
     };
     if (FUSED)
         cmp.load_step(p, qi, lo, min(hi, lo + C::LIST_CAP));
@@ -1025,9 +1082,13 @@ __global__ void __launch_bounds__(128, 2) sa_attn_pair(const AttnParams p) {
             else
                 asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
             lds_barrier();
-            cmp.load_lds(list, c0, c1);
+            if constexpr (PREFILL)
+                cmp.load_lds_prefill(list, c0, c1, lform, p.window);
+            else
+                cmp.load_lds(list, c0, c1);
         }
-        if (FUSED && first_pass && hg == 0 && p.idx_out) cmp.store(p.idx_out + (int64_t)qi * p.topk, c0, c1);
+        if ((FUSED || PREFILL) && first_pass && hg == 0 && p.idx_out)
+            cmp.store(p.idx_out + (int64_t)qi * p.topk, c0, c1);
         const int nv = cmp.pack(p.rows, list, wcnt);
         const int nst = (nv + C::ROWS - 1) / C::ROWS;
         if (c0 == lo && first_pass) {
@@ -1270,9 +1331,10 @@ __global__ void __launch_bounds__(256, 1) sa_attn_decode(const AttnParams p) {
     const int eoff = C::RPW * wave + (lane & 15);
     // (a readable dummy for a load whose value is not needed: the sink)
     const int32_t *dummy = reinterpret_cast<const int32_t *>(p.sink);
+    const ListForm lform = list_form<false>(p, qi);
     auto fetch_stage = [&](int j) -> int {
         const int e = lo + j * C::ROWS + eoff;
-        return e < hi ? step_entry(p, qi, e) : -1;
+        return e < hi ? step_entry(p, lform, qi, e) : -1;
     };
     // An index-list entry fetched ahead inside the stage loop is split into its
     // load (load_entry, from a clamped address so that the load is unconditional)
@@ -1829,7 +1891,7 @@ hipError_t launch_wide(const AttnParams &p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int D, bool FUSED>
+template <int D, int MODE>
 hipError_t launch_pair(const AttnParams &p0, hipStream_t stream) {
     AttnParams p = p0;
     const int cus = cu_count();
@@ -1838,17 +1900,17 @@ hipError_t launch_pair(const AttnParams &p0, hipStream_t stream) {
     const int per_wg = std::min(p.topk, p.split_len);
     if (per_wg <= kPairShortList) {
         if (p.n_sp > 1)
-            hipLaunchKernelGGL((sa_attn_pair<D, kPairShortList, FUSED, true>), dim3((unsigned)p.total_wg), dim3(128),
+            hipLaunchKernelGGL((sa_attn_pair<D, kPairShortList, MODE, true>), dim3((unsigned)p.total_wg), dim3(128),
                                0, stream, p);
         else
-            hipLaunchKernelGGL((sa_attn_pair<D, kPairShortList, FUSED, false>), dim3((unsigned)p.total_wg),
+            hipLaunchKernelGGL((sa_attn_pair<D, kPairShortList, MODE, false>), dim3((unsigned)p.total_wg),
                                dim3(128), 0, stream, p);
     } else {
         if (p.n_sp > 1)
-            hipLaunchKernelGGL((sa_attn_pair<D, kPairLongList, FUSED, true>), dim3((unsigned)p.total_wg), dim3(128),
+            hipLaunchKernelGGL((sa_attn_pair<D, kPairLongList, MODE, true>), dim3((unsigned)p.total_wg), dim3(128),
                                0, stream, p);
         else
-            hipLaunchKernelGGL((sa_attn_pair<D, kPairLongList, FUSED, false>), dim3((unsigned)p.total_wg),
+            hipLaunchKernelGGL((sa_attn_pair<D, kPairLongList, MODE, false>), dim3((unsigned)p.total_wg),
                                dim3(128), 0, stream, p);
     }
     return hipGetLastError();
@@ -1872,8 +1934,20 @@ hipError_t launch_combine(const AttnParams &p, hipStream_t stream) {
 
 bool valid_d(int32_t d) { return d == 64 || d == 128 || d == 256 || d == 512; }
 
-template <bool FUSED, bool KV8>
+// MODE: 0 the index list from memory, 1 the decode step's list built in the
+// kernel, 2 the prefill list built in the kernel (the pair kernel only).
+template <int MODE, bool KV8>
 hipError_t launch_attn(const AttnParams &p, const Variant &v, int32_t d, hipStream_t hs) {
+    constexpr bool FUSED = MODE == 1;
+    if constexpr (MODE == 2) {
+        if (KV8 || v.kernel != SA_KERNEL_PAIR) return hipErrorNotSupported;  // (run_prefill_step asks for it)
+        switch (d) {
+            case 64: return launch_pair<64, 2>(p, hs);
+            case 128: return launch_pair<128, 2>(p, hs);
+            case 256: return launch_pair<256, 2>(p, hs);
+            default: return launch_pair<512, 2>(p, hs);
+        }
+    }
     if (v.kernel == SA_KERNEL_DECODE) {
         switch (d) {
             case 64: return launch_decode<64, FUSED, KV8>(p, hs);
@@ -1885,10 +1959,10 @@ hipError_t launch_attn(const AttnParams &p, const Variant &v, int32_t d, hipStre
     if (KV8) return hipErrorNotSupported;  // (resolve_variant keeps kv8 on the decode kernel)
     if (v.kernel == SA_KERNEL_PAIR) {
         switch (d) {
-            case 64: return launch_pair<64, FUSED>(p, hs);
-            case 128: return launch_pair<128, FUSED>(p, hs);
-            case 256: return launch_pair<256, FUSED>(p, hs);
-            default: return launch_pair<512, FUSED>(p, hs);
+            case 64: return launch_pair<64, MODE>(p, hs);
+            case 128: return launch_pair<128, MODE>(p, hs);
+            case 256: return launch_pair<256, MODE>(p, hs);
+            default: return launch_pair<512, MODE>(p, hs);
         }
     }
     switch (d) {
@@ -1933,7 +2007,7 @@ AttnParams base_params(const uint16_t *q, const uint16_t *kv, const float *sink,
     return p;
 }
 
-template <bool FUSED, bool KV8>
+template <int MODE, bool KV8>
 sa_status enqueue(AttnParams &p, const Variant &v, int32_t d, hipStream_t hs) {
     // decode kernel: one block per workgroup; wide and pair kernels: 8 * ceil(nq / 8) queries' worth
     // wide and pair kernels: queries dealt to the XCDs in runs (see wide_unit) --
@@ -1945,7 +2019,7 @@ sa_status enqueue(AttnParams &p, const Variant &v, int32_t d, hipStream_t hs) {
     const int64_t total = units * p.n_hg * v.n_sp;
     if (total > 0x7fffffffLL) return SA_ERR_SHAPE;
     p.total_wg = (int32_t)total;
-    if (launch_attn<FUSED, KV8>(p, v, d, hs) != hipSuccess) return SA_ERR_HIP;
+    if (launch_attn<MODE, KV8>(p, v, d, hs) != hipSuccess) return SA_ERR_HIP;
     if (v.n_sp > 1 && launch_combine_d(p, d, hs) != hipSuccess) return SA_ERR_HIP;
     return SA_OK;
 }
@@ -2023,8 +2097,8 @@ sa_status run_sparse_attn(const uint16_t *q, const KvRows &kv, const float *sink
     p.kv8s = kv.ks;
     p.idx = idx;
     set_rope(p, rope);
-    return kv.kv8() ? enqueue<false, true>(p, v, d, (hipStream_t)stream)
-                    : enqueue<false, false>(p, v, d, (hipStream_t)stream);
+    return kv.kv8() ? enqueue<0, true>(p, v, d, (hipStream_t)stream)
+                    : enqueue<0, false>(p, v, d, (hipStream_t)stream);
 }
 
 // Fused decode step: ring write of the new row (fp8 round trip), the window list,
@@ -2067,8 +2141,41 @@ sa_status run_decode_step(const uint16_t *q, const KvRows &kv, const uint16_t *k
     p.wbase = (int32_t)((start_pos + 1) % window);
     p.new_slot = (int32_t)(start_pos % window);
     set_rope(p, rope);
-    return kv.kv8() ? enqueue<true, true>(p, v, d, (hipStream_t)stream)
-                    : enqueue<true, false>(p, v, d, (hipStream_t)stream);
+    return kv.kv8() ? enqueue<1, true>(p, v, d, (hipStream_t)stream)
+                    : enqueue<1, false>(p, v, d, (hipStream_t)stream);
+}
+
+// Prefill in one attention launch: the window list and the compressed append
+// built inside the pair kernel (its own instance; the chunk's fp8 round trip,
+// which every query's rows need first, is the caller's separate launch).
+sa_status run_prefill_step(const uint16_t *q, const uint16_t *kv, const float *sink, const int32_t *cidx,
+                           int32_t *idx_out, int64_t b, int64_t s, int32_t h, int32_t d, int64_t rows,
+                           int32_t window, int32_t kc, float scale, uint16_t *out, void *workspace,
+                           size_t workspace_bytes, void *stream, int32_t kernel, int32_t splits) {
+    if (b < 0 || s < 0 || h < 0 || d < 0 || rows < 0 || window <= 0 || kc < 0) return SA_ERR_SHAPE;
+    if (!valid_d(d)) return SA_ERR_UNSUPPORTED;
+    if (!mul_le(b, s, 0x7fffffffLL)) return SA_ERR_SHAPE;
+    const int64_t nq = b * s;
+    if (rows < s || rows > 0x7fffffffLL || s > 0x7fffffffLL) return SA_ERR_SHAPE;
+    const int32_t wcols = (int32_t)(s < window ? s : window);
+    if ((int64_t)wcols + kc > 0x7fffffffLL) return SA_ERR_SHAPE;
+    if (nq == 0 || h == 0) return SA_OK;
+    if (!q || !kv || !sink || !out || (kc > 0 && !cidx)) return SA_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(kv) | reinterpret_cast<uintptr_t>(out)) % 16)
+        return SA_ERR_SHAPE;
+    if (kernel != 0 && kernel != SA_KERNEL_PAIR) return SA_ERR_UNSUPPORTED;  // the pair kernel builds this list
+    const int32_t topk = wcols + kc;
+    Variant v;
+    sa_status st = resolve_variant(nq, h, topk, SA_KERNEL_PAIR, splits, &v);
+    if (st != SA_OK) return st;
+    if ((st = check_workspace(v, nq, h, d, workspace, workspace_bytes)) != SA_OK) return st;
+    AttnParams p = base_params(q, kv, sink, nq, s, h, d, rows, topk, scale, out, workspace, v);
+    p.cidx = cidx;
+    p.idx_out = idx_out;
+    p.pos = -1;  // the prefill list
+    p.window = wcols;
+    p.kc = kc;
+    return enqueue<2, false>(p, v, d, (hipStream_t)stream);
 }
 
 KvRows bf16_rows(const uint16_t *kv) {
@@ -2184,6 +2291,28 @@ extern "C" sa_status sa_sparse_attn_decode_step(const uint16_t *q, uint16_t *kv,
                                                 int32_t kernel, int32_t splits) {
     return run_decode_step(q, bf16_rows(kv), kv_new, sink, cidx, idx_out, b, h, d, rows, window, kc, start_pos,
                            scale, out, workspace, workspace_bytes, stream, kernel, splits);
+}
+
+extern "C" size_t sa_sparse_attn_prefill_step_workspace_bytes(int64_t b, int64_t s, int32_t h, int32_t d,
+                                                              int32_t window, int32_t kc, int32_t kernel,
+                                                              int32_t splits) {
+    if (b < 0 || s < 0 || h <= 0 || window <= 0 || kc < 0 || !valid_d(d) || !mul_le(b, s, 0x7fffffffLL)) return 0;
+    const int64_t wcols = s < window ? s : window;
+    if (wcols + kc > 0x7fffffffLL) return 0;
+    if (kernel != 0 && kernel != SA_KERNEL_PAIR) return 0;
+    Variant v;
+    if (resolve_variant(b * s, h, (int32_t)(wcols + kc), SA_KERNEL_PAIR, splits, &v) != SA_OK) return 0;
+    return workspace_for(v, b * s, h, d);
+}
+
+extern "C" sa_status sa_sparse_attn_prefill_step(const uint16_t *q, const uint16_t *kv, const float *sink,
+                                                 const int32_t *cidx, int32_t *idx_out, int64_t b, int64_t s,
+                                                 int32_t h, int32_t d, int64_t rows, int32_t window, int32_t kc,
+                                                 float scale, uint16_t *out, void *workspace,
+                                                 size_t workspace_bytes, void *stream, int32_t kernel,
+                                                 int32_t splits) {
+    return run_prefill_step(q, kv, sink, cidx, idx_out, b, s, h, d, rows, window, kc, scale, out, workspace,
+                            workspace_bytes, stream, kernel, splits);
 }
 
 extern "C" size_t sa_sparse_attn_kv8_workspace_bytes(int64_t b, int64_t s, int32_t h, int32_t d, int32_t topk,

@@ -27,6 +27,7 @@ import torch
 
 from . import sparse_attn, window_kv_update, window_topk_idxs, append_compressed_idxs, act_quant_fp8_
 from . import workspace_bytes, sparse_attn_decode_step, decode_step_workspace_bytes
+from . import sparse_attn_prefill_step, prefill_step_workspace_bytes
 from . import kv8_pack, kv8_workspace_bytes, sparse_attn_decode_step_kv8
 from .workloads import WORKLOADS, rope_table
 
@@ -67,6 +68,8 @@ def prepare(wid: int, raw: dict, device: str = "cuda", kv8: bool = False, rope_d
     nws = workspace_bytes(w.b, w.s, w.h, w.d, w.topk)
     if w.start_pos > 0:
         nws = max(nws, decode_step_workspace_bytes(w.b, w.h, w.d, w.window, w.n_comp))
+    else:
+        nws = max(nws, prefill_step_workspace_bytes(w.b, w.s, w.h, w.d, w.window, w.n_comp))
     if kv8:
         st.kc, st.ks = kv8_pack(st.kv)                     # the cache held as codes + scale records
         st.kv = None
@@ -134,6 +137,22 @@ def step_fused(st: SimpleNamespace) -> torch.Tensor:
     return sparse_attn_decode_step(st.q, st.kv, st.new_rows.view(w.b, w.d), st.sink, w.window, w.start_pos,
                                    w.scale, cidx=st.comp.view(w.b, w.n_comp) if st.comp is not None else None,
                                    out=st.out, idx_out=st.idx, workspace=st.ws, rope=st.rope)
+
+
+def attend_fused_prefill(st: SimpleNamespace) -> torch.Tensor:
+    """Step 4 of a prefill with steps 2-3 inside it (sa_sparse_attn_prefill_step):
+    the window list and the compressed append are built in the attention kernel."""
+    w = st.w
+    assert w.start_pos == 0, "the prefill list starts at position 0"
+    return sparse_attn_prefill_step(st.q, st.kv, st.sink, w.window, w.scale, cidx=st.comp, out=st.out,
+                                    workspace=st.ws)
+
+
+def step_fused_prefill(st: SimpleNamespace) -> torch.Tensor:
+    """A prefill step in two launches: the chunk's fp8 round trip (and its last rows
+    into the ring), then the attention with the list built inside it."""
+    window_kv_update(st.ring, st.chunk, 0)
+    return attend_fused_prefill(st)
 
 
 def step_fused_kv8(st: SimpleNamespace) -> torch.Tensor:

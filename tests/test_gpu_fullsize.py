@@ -6,8 +6,9 @@
    decode + compressed (batch 128, 128 heads, 128 + 2048 entries);
  * the separate-call step (ring update with the fp8 round trip, window lists,
    compressed append, attention, with and without the fused output rotation)
-   at the prefill workloads' full shapes: 4096 queries (window only) and 8192
-   queries (window + compressed).
+   and the prefill step with the lists built in the attention kernel
+   (sa_sparse_attn_prefill_step) at the prefill workloads' full shapes: 4096
+   queries (window only) and 8192 queries (window + compressed).
 
 Each runs through `pipeline`, the functions the benchmark calls, with the same
 buffers and launch configuration.  Before the step every output element is
@@ -145,7 +146,7 @@ def test_decode_step_full_size(wid, kind):
     compare_out(got, ref32, f"workload {wid} {kind}", rope=rope, q_chunk=1)
 
 
-PREFILL_CASES = [(3, "bf16"), (3, "rope"), (5, "bf16"), (5, "rope")]
+PREFILL_CASES = [(3, "bf16"), (3, "rope"), (3, "fused"), (5, "bf16"), (5, "rope"), (5, "fused")]
 
 
 @pytest.mark.parametrize("wid,kind", PREFILL_CASES, ids=[f"w{w}-{k}" for w, k in PREFILL_CASES])
@@ -157,7 +158,7 @@ def test_prefill_step_full_size(wid, kind):
     st.out.view(torch.int16).fill_(BF16_NAN)
     st.idx.fill_(-7)
     st.ring.view(torch.int16).fill_(BF16_NAN)     # every slot is written: the chunk outlasts the ring
-    out = pipeline.step(st)
+    out = pipeline.step_fused_prefill(st) if kind == "fused" else pipeline.step(st)
     torch.cuda.synchronize()
     say(f"workload {wid} {kind}: GPU step done, oracle running")
 
@@ -168,7 +169,10 @@ def test_prefill_step_full_size(wid, kind):
     oracle.ring_write(ring_ref, np.ascontiguousarray(kv_ref[:, : w.win_rows]), 0)
     assert np.array_equal(bits(st.ring), ring_ref), "ring after the prefill"
     idx_ref = oracle_lists(w, raw["comp"])
-    assert np.array_equal(st.idx.cpu().numpy(), idx_ref), "index lists"
+    if kind == "fused":       # the lists stay inside the attention kernel
+        assert bool((st.idx == -7).all()), "the fused step writes no index list"
+    else:
+        assert np.array_equal(st.idx.cpu().numpy(), idx_ref), "index lists"
     _, ref32 = oracle.sparse_attn(bits(raw["q"]), kv_ref, raw["sink"].numpy(), idx_ref, w.scale, want_f32=True)
     say(f"workload {wid} {kind}: oracle done, comparing")
     rope = (st.rope[0].cpu().numpy(), st.rope[1], 0) if kind == "rope" else None
