@@ -6,10 +6,9 @@ KV rows rounded through fp8 and written into the window ring, the window slot
 lists built, compressed positions appended (when the workload has them) and
 the sparse attention itself -- all through the C ABI on one stream.  Decode
 workloads run the step as one launch (sa_sparse_attn_decode_step, the lists
-built inside the attention kernel); ``--unfused`` times the separate calls.
-Prefill workloads run the separate calls; ``--prefill-list-in-kernel`` runs
-them as two launches instead (the chunk's fp8 round trip, then
-sa_sparse_attn_prefill_step with the lists built inside the attention kernel).
+built inside the attention kernel); prefill workloads as two (the chunk's fp8
+round trip, then sa_sparse_attn_prefill_step with the lists built inside the
+attention kernel); ``--unfused`` times the separate calls.
 ``--kv8`` holds the decode cache fp8-resident (e4m3fn codes + E8M0 block
 scales) and runs the one-launch step on it: the same results, bit for bit,
 from about half the gathered bytes.  ``--rope`` fuses the output's inverse
@@ -74,11 +73,8 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration under rocprofv3)")
     ap.add_argument("--unfused", action="store_true",
-                    help="decode: run the step as separate calls (ring update, lists, attention) "
-                         "instead of the one-launch decode step")
-    ap.add_argument("--prefill-list-in-kernel", action="store_true",
-                    help="prefill: build the index lists inside the attention kernel "
-                         "(sa_sparse_attn_prefill_step) instead of the separate list calls")
+                    help="run the step as separate calls (ring update, lists, attention) instead of "
+                         "building the lists inside the attention kernel")
     ap.add_argument("--kv8", action="store_true",
                     help="decode: the cache held fp8-resident (e4m3fn codes + E8M0 block scales) and read "
                          "and written in that form by the one-launch step (bitwise the same results)")
@@ -433,13 +429,10 @@ def main():
     sets = [pipeline.prepare(args.workload, raw0, kv8=args.kv8, rope_dim=rope_dim)]
     pipeline.build_index(sets[0])
     torch.cuda.synchronize()
-    # decode: the one-launch step unless --unfused; prefill: the separate calls
-    # unless --prefill-list-in-kernel (without the output rotation)
-    if args.prefill_list_in_kernel and (w.start_pos > 0 or rope_dim or args.unfused):
-        print("bench.py: --prefill-list-in-kernel applies to the prefill workloads (3, 5), without --rope",
-              file=sys.stderr)
-        sys.exit(2)
-    fused = (w.start_pos > 0 and not args.unfused) or args.prefill_list_in_kernel
+    # the lists built in the attention kernel unless --unfused (a prefill with the
+    # output rotation fused runs the separate calls: the prefill list has no
+    # rotating epilogue of its own)
+    fused = not args.unfused and (w.start_pos > 0 or not rope_dim)
     if args.kv8:
         step_fn = kern_fn = pipeline.step_fused_kv8
     elif w.start_pos > 0:
@@ -540,8 +533,7 @@ def main():
         achieved = work["flops"] / (attn_mean / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
-    tag = traffic_tag(args.workload, fused or w.start_pos == 0, args.kv8, rope_dim)
-    roof["traffic"] = measured_traffic(tag + ("_inlist" if args.prefill_list_in_kernel else ""))
+    roof["traffic"] = measured_traffic(traffic_tag(args.workload, fused, args.kv8, rope_dim))
     roof["algorithmic_bytes"] = work["bytes"]
     roof["algorithmic_flops"] = work["flops"]
     roof["kernel_ms_mean"] = round(attn_mean, 5)

@@ -377,14 +377,15 @@ struct Compactor {
         }
     }
 
-    // prefill list: the window entries by formula, the compressed ones from
-    // list[] (raw positions copied there directly, entry e at list[e - c0])
-    __device__ __forceinline__ void load_lds_prefill(const int *list, int c0, int c1, const ListForm &f,
-                                                     int window) {
+    // prefill list from list[] (entry e at list[e - c0]): the window entries as
+    // stored, the compressed positions (copied there raw) shifted past the chunk's
+    // s rows, -1 kept
+    __device__ __forceinline__ void load_lds_prefill(const int *list, int c0, int c1, int window, int s) {
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int e = c0 + k * NT + (int)threadIdx.x;
-            v[k] = e >= c1 ? -1 : (e < window ? window_entry(f, e) : compressed_entry(f, list[e - c0]));
+            const int raw = e < c1 ? list[e - c0] : -1;
+            v[k] = e >= c1 ? -1 : (e < window || raw < 0 ? raw : (int)((uint32_t)raw + (uint32_t)s));
         }
     }
 
@@ -984,7 +985,6 @@ __global__ void __launch_bounds__(128, 2) sa_attn_pair(const AttnParams p) {
     const int hi = min(p.topk, lo + p.split_len);
     const int32_t *idxq = MODE == 0 ? p.idx + (int64_t)qi * p.topk : nullptr;
     const int32_t *cq = PREFILL ? p.cidx + (int64_t)qi * p.kc - p.window : nullptr;  // entry e >= window: cq[e]
-    const ListForm lform = list_form<PREFILL>(p, qi);
     const bool has_new = FUSED && p.window - 1 >= lo && p.window - 1 < hi;
     u32x4_t new_raw = {0u, 0u, 0u, 0u};
     if (has_new && wave == 0 && chunk_lane)
@@ -1004,6 +1004,10 @@ __global__ void __launch_bounds__(128, 2) sa_attn_pair(const AttnParams p) {
 #pragma unroll 1
             for (int e0 = max(c0, p.window) + wave * 64; e0 < c1; e0 += C::THREADS)
                 if (e0 + lane < c1) dma_4B(cq + e0 + lane, list_base + (uint32_t)(e0 - c0) * 4);
+            // the window entries by formula, stored beside them (the barrier before
+            // the read-back publishes both)
+            const ListForm f = list_form<true>(p, qi);
+            for (int e = c0 + tid; e < min(c1, p.window); e += C::THREADS) list[e - c0] = window_entry(f, e);
         } else {
 #pragma unroll 1
             for (int e0 = c0 + wave * 64; e0 < c1; e0 += C::THREADS)
@@ -1083,7 +1087,7 @@ __global__ void __launch_bounds__(128, 2) sa_attn_pair(const AttnParams p) {
                 asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
             lds_barrier();
             if constexpr (PREFILL)
-                cmp.load_lds_prefill(list, c0, c1, lform, p.window);
+                cmp.load_lds_prefill(list, c0, c1, p.window, p.s);
             else
                 cmp.load_lds(list, c0, c1);
         }
