@@ -429,10 +429,8 @@ def main():
     sets = [pipeline.prepare(args.workload, raw0, kv8=args.kv8, rope_dim=rope_dim)]
     pipeline.build_index(sets[0])
     torch.cuda.synchronize()
-    # the lists built in the attention kernel unless --unfused (a prefill with the
-    # output rotation fused runs the separate calls: the prefill list has no
-    # rotating epilogue of its own)
-    fused = not args.unfused and (w.start_pos > 0 or not rope_dim)
+    # the lists built in the attention kernel unless --unfused
+    fused = not args.unfused
     if args.kv8:
         step_fn = kern_fn = pipeline.step_fused_kv8
     elif w.start_pos > 0:

@@ -418,11 +418,12 @@ sa_status sa_apply_rotary(uint16_t *x, int64_t b, int64_t s, int32_t h, int32_t 
  * (apply_rotary_emb(o[..., -rd:], freqs_cis, inverse=True)).
  *
  * Same result, bit for bit, as the unfused pair of calls
- *   sa_sparse_attn_ex(..., kernel, splits)   (resp. sa_sparse_attn_decode_step)
+ *   sa_sparse_attn_ex(..., kernel, splits)   (resp. sa_sparse_attn_decode_step,
+ *                                             sa_sparse_attn_prefill_step)
  *   sa_apply_rotary(out, b, s, h, d, rope_dim, rope_table, n_pos, start_pos, 1)
  * (the rounded bf16 output is rotated, as the pages round before rotating),
  * without the second pass over the output.  Query si of a sequence sits at
- * position start_pos + si (the decode step: start_pos).  rope_table as for
+ * position start_pos + si (the decode step: start_pos; the prefill step: si).  rope_table as for
  * sa_apply_rotary, 16-byte aligned; rope_dim a multiple of 8 in [8, d];
  * positions within [0, n_pos) (else SA_ERR_SHAPE); NULL rope_table:
  * SA_ERR_NULL.  Other arguments, workspace and errors as for the unfused
@@ -439,6 +440,13 @@ sa_status sa_sparse_attn_decode_step_rope(const uint16_t *q, uint16_t *kv, const
                                           int64_t start_pos, float scale, uint16_t *out, void *workspace,
                                           size_t workspace_bytes, void *stream, int32_t kernel, int32_t splits,
                                           const float *rope_table, int64_t n_pos, int32_t rope_dim);
+
+sa_status sa_sparse_attn_prefill_step_rope(const uint16_t *q, const uint16_t *kv, const float *sink,
+                                           const int32_t *cidx, int32_t *idx_out, int64_t b, int64_t s, int32_t h,
+                                           int32_t d, int64_t rows, int32_t window, int32_t kc, float scale,
+                                           uint16_t *out, void *workspace, size_t workspace_bytes, void *stream,
+                                           int32_t kernel, int32_t splits, const float *rope_table, int64_t n_pos,
+                                           int32_t rope_dim);
 
 /* ------------------------------------------------------------------------
  * The indexer's selection tail -- [INDEXER] Indexer.forward after the scores

@@ -90,12 +90,14 @@ def lib() -> ctypes.CDLL:
         L.sa_sparse_attn_prefill_step_workspace_bytes.restype = sz
         L.sa_sparse_attn_prefill_step.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i64, i32, i32, f32, vp,
                                                   vp, sz, vp, i32, i32]
+        L.sa_sparse_attn_prefill_step_rope.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i64, i32, i32, f32,
+                                                       vp, vp, sz, vp, i32, i32, vp, i64, i32]
         for fn in ("sa_window_topk_idxs_shape", "sa_window_topk_idxs", "sa_append_compressed_idxs",
                    "sa_act_quant_fp8_inplace", "sa_window_kv_update", "sa_sparse_attn", "sa_sparse_attn_ex",
                    "sa_sparse_attn_decode_step", "sa_kv8_pack", "sa_kv8_unpack", "sa_sparse_attn_kv8",
                    "sa_sparse_attn_decode_step_kv8", "sa_apply_rotary", "sa_sparse_attn_rope",
                    "sa_sparse_attn_decode_step_rope", "sa_indexer_topk", "sa_sparse_attn_noalloc",
-                   "sa_sparse_attn_prefill_step"):
+                   "sa_sparse_attn_prefill_step", "sa_sparse_attn_prefill_step_rope"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -334,13 +336,14 @@ def prefill_step_workspace_bytes(b: int, s: int, h: int, d: int, window: int, kc
 def sparse_attn_prefill_step(q: torch.Tensor, kv: torch.Tensor, sink: torch.Tensor, window: int, scale: float,
                              cidx: torch.Tensor | None = None, out: torch.Tensor | None = None,
                              idx_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                             variant: tuple | None = None, stream=None) -> torch.Tensor:
+                             variant: tuple | None = None, stream=None, rope: tuple | None = None) -> torch.Tensor:
     """Prefill attention with the index list built in the kernel: q [b][s][h][d] at
     positions 0 .. s-1, kv [b][rows][d] (rows [0, s) the chunk, already through its
     fp8 round trip; compressed rows after), the window list (min(s, window)
     columns) + cidx [b][s][kc] (+s) as the index list, built by the pair kernel
     (``variant`` may only name it).  ``idx_out`` ([b][s][min(s, window) + kc]
-    int32) receives the list when given."""
+    int32) receives the list when given.  ``rope`` = (table, rope_dim) un-rotates
+    the output's last rope_dim values at each query's position."""
     _dev(q, "q", torch.bfloat16)
     _dev(kv, "kv", torch.bfloat16)
     _dev(sink, "sink", torch.float32)
@@ -369,12 +372,16 @@ def sparse_attn_prefill_step(q: torch.Tensor, kv: torch.Tensor, sink: torch.Tens
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check("sa_sparse_attn_prefill_step",
-           lib().sa_sparse_attn_prefill_step(q.data_ptr(), kv.data_ptr(), sink.data_ptr(),
-                                             cidx.data_ptr() if cidx is not None else None,
-                                             idx_out.data_ptr() if idx_out is not None else None, b, s, h, d, rows,
-                                             window, kc, float(scale), out.data_ptr(), ws_ptr, ws_bytes,
-                                             _stream(stream), k, sp))
+    args = (q.data_ptr(), kv.data_ptr(), sink.data_ptr(), cidx.data_ptr() if cidx is not None else None,
+            idx_out.data_ptr() if idx_out is not None else None, b, s, h, d, rows, window, kc, float(scale),
+            out.data_ptr(), ws_ptr, ws_bytes, _stream(stream), k, sp)
+    if rope is not None:
+        table, rope_dim = rope
+        _dev(table, "rope table", torch.float32)
+        _check("sa_sparse_attn_prefill_step_rope",
+               lib().sa_sparse_attn_prefill_step_rope(*args, table.data_ptr(), table.shape[0], rope_dim))
+        return out
+    _check("sa_sparse_attn_prefill_step", lib().sa_sparse_attn_prefill_step(*args))
     return out
 
 

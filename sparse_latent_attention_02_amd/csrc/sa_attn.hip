@@ -2155,9 +2155,12 @@ sa_status run_decode_step(const uint16_t *q, const KvRows &kv, const uint16_t *k
 sa_status run_prefill_step(const uint16_t *q, const uint16_t *kv, const float *sink, const int32_t *cidx,
                            int32_t *idx_out, int64_t b, int64_t s, int32_t h, int32_t d, int64_t rows,
                            int32_t window, int32_t kc, float scale, uint16_t *out, void *workspace,
-                           size_t workspace_bytes, void *stream, int32_t kernel, int32_t splits) {
+                           size_t workspace_bytes, void *stream, int32_t kernel, int32_t splits,
+                           Rope rope = Rope()) {
     if (b < 0 || s < 0 || h < 0 || d < 0 || rows < 0 || window <= 0 || kc < 0) return SA_ERR_SHAPE;
     if (!valid_d(d)) return SA_ERR_UNSUPPORTED;
+    rope.pos0 = 0;
+    if (check_rope(rope, d, s) != SA_OK) return SA_ERR_SHAPE;
     if (!mul_le(b, s, 0x7fffffffLL)) return SA_ERR_SHAPE;
     const int64_t nq = b * s;
     if (rows < s || rows > 0x7fffffffLL || s > 0x7fffffffLL) return SA_ERR_SHAPE;
@@ -2179,6 +2182,7 @@ sa_status run_prefill_step(const uint16_t *q, const uint16_t *kv, const float *s
     p.pos = -1;  // the prefill list
     p.window = wcols;
     p.kc = kc;
+    set_rope(p, rope);
     return enqueue<2, false>(p, v, d, (hipStream_t)stream);
 }
 
@@ -2317,6 +2321,22 @@ extern "C" sa_status sa_sparse_attn_prefill_step(const uint16_t *q, const uint16
                                                  int32_t splits) {
     return run_prefill_step(q, kv, sink, cidx, idx_out, b, s, h, d, rows, window, kc, scale, out, workspace,
                             workspace_bytes, stream, kernel, splits);
+}
+
+extern "C" sa_status sa_sparse_attn_prefill_step_rope(const uint16_t *q, const uint16_t *kv, const float *sink,
+                                                      const int32_t *cidx, int32_t *idx_out, int64_t b, int64_t s,
+                                                      int32_t h, int32_t d, int64_t rows, int32_t window,
+                                                      int32_t kc, float scale, uint16_t *out, void *workspace,
+                                                      size_t workspace_bytes, void *stream, int32_t kernel,
+                                                      int32_t splits, const float *rope_table, int64_t n_pos,
+                                                      int32_t rope_dim) {
+    if (!rope_table) return SA_ERR_NULL;
+    Rope r;
+    r.table = rope_table;
+    r.n_pos = n_pos;
+    r.dim = rope_dim;
+    return run_prefill_step(q, kv, sink, cidx, idx_out, b, s, h, d, rows, window, kc, scale, out, workspace,
+                            workspace_bytes, stream, kernel, splits, r);
 }
 
 extern "C" size_t sa_sparse_attn_kv8_workspace_bytes(int64_t b, int64_t s, int32_t h, int32_t d, int32_t topk,

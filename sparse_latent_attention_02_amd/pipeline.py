@@ -145,7 +145,7 @@ def attend_fused_prefill(st: SimpleNamespace) -> torch.Tensor:
     w = st.w
     assert w.start_pos == 0, "the prefill list starts at position 0"
     return sparse_attn_prefill_step(st.q, st.kv, st.sink, w.window, w.scale, cidx=st.comp, out=st.out,
-                                    workspace=st.ws)
+                                    workspace=st.ws, rope=st.rope)
 
 
 def step_fused_prefill(st: SimpleNamespace) -> torch.Tensor:

@@ -146,7 +146,8 @@ def test_decode_step_full_size(wid, kind):
     compare_out(got, ref32, f"workload {wid} {kind}", rope=rope, q_chunk=1)
 
 
-PREFILL_CASES = [(3, "bf16"), (3, "rope"), (3, "fused"), (5, "bf16"), (5, "rope"), (5, "fused")]
+PREFILL_CASES = [(3, "bf16"), (3, "rope"), (3, "fused"), (3, "fused-rope"), (5, "bf16"), (5, "rope"), (5, "fused"),
+                 (5, "fused-rope")]
 
 
 @pytest.mark.parametrize("wid,kind", PREFILL_CASES, ids=[f"w{w}-{k}" for w, k in PREFILL_CASES])
@@ -154,11 +155,12 @@ def test_prefill_step_full_size(wid, kind):
     w = wl.WORKLOADS[wid]
     say(f"prefill step, workload {wid} ({w.name}), {kind}: preparing")
     raw = raw_inputs(wid)
-    st = pipeline.prepare(wid, raw, rope_dim=pipeline.ROPE_DIM if kind == "rope" else 0)
+    rotated, fused = kind in ("rope", "fused-rope"), kind.startswith("fused")
+    st = pipeline.prepare(wid, raw, rope_dim=pipeline.ROPE_DIM if rotated else 0)
     st.out.view(torch.int16).fill_(BF16_NAN)
     st.idx.fill_(-7)
     st.ring.view(torch.int16).fill_(BF16_NAN)     # every slot is written: the chunk outlasts the ring
-    out = pipeline.step_fused_prefill(st) if kind == "fused" else pipeline.step(st)
+    out = pipeline.step_fused_prefill(st) if fused else pipeline.step(st)
     torch.cuda.synchronize()
     say(f"workload {wid} {kind}: GPU step done, oracle running")
 
@@ -169,11 +171,11 @@ def test_prefill_step_full_size(wid, kind):
     oracle.ring_write(ring_ref, np.ascontiguousarray(kv_ref[:, : w.win_rows]), 0)
     assert np.array_equal(bits(st.ring), ring_ref), "ring after the prefill"
     idx_ref = oracle_lists(w, raw["comp"])
-    if kind == "fused":       # the lists stay inside the attention kernel
+    if fused:                 # the lists stay inside the attention kernel
         assert bool((st.idx == -7).all()), "the fused step writes no index list"
     else:
         assert np.array_equal(st.idx.cpu().numpy(), idx_ref), "index lists"
     _, ref32 = oracle.sparse_attn(bits(raw["q"]), kv_ref, raw["sink"].numpy(), idx_ref, w.scale, want_f32=True)
     say(f"workload {wid} {kind}: oracle done, comparing")
-    rope = (st.rope[0].cpu().numpy(), st.rope[1], 0) if kind == "rope" else None
+    rope = (st.rope[0].cpu().numpy(), st.rope[1], 0) if rotated else None
     compare_out(bits(out), ref32, f"workload {wid} {kind}", rope=rope)

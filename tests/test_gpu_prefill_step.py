@@ -127,3 +127,24 @@ def test_prefill_step_errors():
             sa.sparse_attn_prefill_step(q, torch.zeros((1, 4, 64), dtype=torch.bfloat16, device=DEV), sink, 4, 0.1,
                                         variant=(k, 1))
         assert e.value.status == sa.SA_ERR_UNSUPPORTED
+
+
+def test_prefill_step_with_rotation_matches_separate_calls():
+    """The output's inverse rotation fused into the prefill step: bit for bit the
+    separate calls with the rotation fused into sa_sparse_attn (itself checked
+    against the oracle's exact rotation)."""
+    from sparse_latent_attention_02_amd.workloads import rope_table
+    c = make_case(21, 2, 200, 32, 512, 64, 150, 80)
+    b, s, W, kc, d = 2, 200, 64, 80, 512
+    table = rope_table(77, s, 64).to(DEV)
+    variant = (sa.SA_KERNEL_PAIR, 1)                 # one variant on both sides: the same arithmetic
+    out = sa.sparse_attn_prefill_step(c["q"].to(DEV), c["kv"].to(DEV), c["sink"].to(DEV), W, d ** -0.5,
+                                      cidx=c["cidx"].to(DEV), rope=(table, 64), variant=variant)
+    idx = torch.full((b, s, min(s, W) + kc), -7, dtype=torch.int32, device=DEV)
+    sa.window_topk_idxs(W, b, s, 0, out=idx)
+    sa.append_compressed_idxs(idx, min(s, W), c["cidx"].to(DEV), s)
+    ref = sa.sparse_attn(c["q"].to(DEV), c["kv"].to(DEV), c["sink"].to(DEV), idx, d ** -0.5, rope=(table, 64, 0),
+                         variant=variant)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
