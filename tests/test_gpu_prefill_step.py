@@ -85,6 +85,7 @@ CASES = [
     (3, 1, 257, 8, 64, 128, 0, 0),         # window only
     (4, 3, 33, 24, 256, 16, 500, 180),     # ragged heads, long compressed part
     (5, 1, 1, 4, 512, 8, 10, 5),           # a single query
+    (6, 1, 70, 16, 128, 64, 3000, 2500),   # 2564-entry lists: compacted in two chunks
 ]
 
 
