@@ -149,3 +149,28 @@ def test_prefill_step_with_rotation_matches_separate_calls():
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
 
+
+
+@pytest.mark.parametrize("d", [64, 512])
+def test_prefill_step_scores_outrunning_the_first_stage(d):
+    """The pair kernel takes the weights against the first stage max it sees and
+    replays the list (copied again from memory, window entries formed again) when
+    a later stage outruns it by too much.  Two compressed rows built from query 3's
+    head row 5 sit at list entries 130 and 250; the result must still be the plain
+    softmax, dominated there by the second."""
+    g = torch.Generator().manual_seed(78)
+    b, s, h, W, kc = 1, 4, 64, 4, 300
+    q = torch.randn((b, s, h, d), generator=g).to(torch.bfloat16)
+    kv = (0.05 * torch.randn((b, s + kc, d), generator=g)).to(torch.bfloat16)
+    c1 = 60.0 / (d ** 0.5 * 1.4426950408889634)   # log2-domain score about 60 above the rest
+    kv[0, s + 130 - W] = (c1 * q[0, 3, 5].float()).to(torch.bfloat16)
+    kv[0, s + 250 - W] = (2.2 * c1 * q[0, 3, 5].float()).to(torch.bfloat16)
+    cidx = torch.arange(kc, dtype=torch.int32).repeat(b, s, 1).contiguous()
+    sink = torch.randn(h, generator=g)
+    c = dict(q=q, kv=kv, sink=sink, cidx=cidx, W=W, s=s, h=h, d=d, kc=kc)
+    idx_ref, ref = oracle_case(c)
+    idx_got, got = gpu_fused(c)
+    assert np.array_equal(idx_got, idx_ref), "written list"
+    assert_parity(got, ref, f"prefill replay d {d}")
+    r = ref.reshape(b, s, h, d)[0, 3, 5]
+    assert np.allclose(r, kv[0, s + 250 - W].float().numpy(), rtol=2e-2, atol=2e-2)
